@@ -1,0 +1,11 @@
+"""CPU oracle for the BitLinear forward -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  It shares no code with the HIP path.
+"""
+from .bitlinear_oracle import *  # noqa: F401,F403
+from .bitlinear_oracle import (EPS32, absmax_quantize, absmean_gamma, absmean_gamma_fsum,
+                               abs_sum_f64, bitlinear_forward, dequant, exact_abs_sum_units,
+                               forward_from_codes, pack_codes, padded_k, quantize_weights,
+                               sampled_forward, ternary_codes, unpack_codes, zero_gemm,
+                               zero_gemm_dot, zero_gemm_naive)

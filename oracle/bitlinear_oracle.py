@@ -1,0 +1,288 @@
+"""Plain CPU oracle for the BitNet b1.58 BitLinear forward.
+
+TEST INFRASTRUCTURE ONLY.  The tests, the package's smoke check and the
+benchmark's CPU-baseline leg import this module; the product path never does,
+and this module imports nothing from the product package.
+
+It is written to be read against the pages, not to be fast: numpy in float32
+where the method works in float32, float64/exact integers where it
+accumulates, and pure-Python loops for the literal add/subtract/skip form.
+
+Citations
+---------
+[PMV] is the produtoramaxvision.com.br blog article on BitNet b1.58 (ternary
+quantisation, the BitLinear layer and Zero-GEMM).  Its sections:
+
+* [PMV §1]  why 1.58 bits per weight: the AbsMean weight equations (gamma and
+  the RoundClip to {-1, 0, +1}), the reconstruction W_hat = gamma * W_q, and the
+  per-token AbsMax INT8 activation equations;
+* [PMV §2]  how BitLinear removes multiplications (Zero-GEMM): add for +1,
+  subtract for -1, skip for 0, INT32 accumulation, the worked 8-element
+  example, and the single rescale of A_q x W_q^T by gamma_A * gamma / 127;
+* [PMV §3]  the memory wall: 2-bit packing, 0.25 byte per weight.
+
+Readings where the article leaves a step open:
+
+* eps = 1e-5 as a float32 constant, added in float32 (the article names an eps
+  but not its value; 1e-5 is the value the lifelog blog's demo uses).
+* "Round" is round-half-to-even (numpy ``rint``).
+* gamma is per tensor, a float32 result of a float64 accumulation, read as:
+  the sum of |W| is the float64 number nearest the exact sum (what an
+  error-free float64 accumulation gives, i.e. ``math.fsum``), divided by N*K
+  in float64, then rounded to float32.
+* The activation scale is grouped as the article writes it:
+  s = fp32(127 / fp32(gamma_A + eps)), then each code is rint(fp32(x * s)),
+  clipped to [-128, 127].
+* The dequantisation multiplies by gamma_A * gamma / 127 exactly as written
+  (no eps there); this oracle forms it in float64 and rounds once to float32.
+* The 2-bit layout is this library's own encoding (the article fixes only
+  the size, two bits per weight): code c = q + 1 in {0, 1, 2}; rows padded to a
+  multiple of 64 weights with c = 1 (a zero weight); row n is a run of
+  little-endian 32-bit words, word j covers k in [16j, 16j + 16), and bits
+  [8b + 2i, 8b + 2i + 1] of word j hold the code of k = 16j + 4i + b.
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+against the article's worked example, brute force, ``math.fsum``, closed forms
+or invariants; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict
+
+import numpy as np
+
+EPS32 = np.float32(1e-5)
+PAD_MULTIPLE = 64  # packed rows hold a multiple of 64 weights
+
+
+# ---------------------------------------------------------------------------
+# a1: AbsMean scale  [PMV §1, AbsMean equation]
+# ---------------------------------------------------------------------------
+
+def exact_abs_sum_units(W: np.ndarray) -> int:
+    """Exact sum of |W| as a Python integer in units of 2**-149.
+
+    Every finite float32 magnitude is an integer significand times a power of
+    two: |w| = Msig * 2**(s - 149) with s = max(e - 1, 0), where e is the
+    biased exponent field and Msig includes the implicit bit for e >= 1.
+    Significands are summed per exponent (float64 weights in ``bincount`` stay
+    exact because every running total stays below 2**53 for < 2**29 values),
+    then the bins are combined as exact Python integers.
+    """
+    a = np.ascontiguousarray(W, dtype=np.float32).ravel()
+    if a.size >= (1 << 29):
+        raise ValueError("exact_abs_sum_units: more than 2**29 values")
+    if not np.all(np.isfinite(a)):
+        raise ValueError("exact_abs_sum_units: non-finite weight")
+    bits = a.view(np.uint32) & np.uint32(0x7FFFFFFF)
+    e = (bits >> np.uint32(23)).astype(np.int64)
+    m = (bits & np.uint32(0x7FFFFF)).astype(np.int64)
+    sig = np.where(e > 0, m | (1 << 23), m)
+    s = np.maximum(e - 1, 0)
+    bins = np.bincount(s, weights=sig.astype(np.float64), minlength=254)
+    total = 0
+    for shift in np.nonzero(bins)[0]:
+        total += int(bins[shift]) << int(shift)
+    return total
+
+
+def abs_sum_f64(W: np.ndarray) -> float:
+    """The float64 number nearest the exact sum of |W| (round half to even)."""
+    units = exact_abs_sum_units(W)
+    return math.ldexp(float(units), -149) if units else 0.0
+
+
+def absmean_gamma(W: np.ndarray) -> np.float32:
+    """gamma = (1 / (n*m)) * sum |W_ij|  [PMV §1, AbsMean equation], per tensor.
+
+    Accumulation: nearest float64 to the exact sum; float64 division by the
+    element count; one rounding to float32.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    if W.size == 0:
+        raise ValueError("absmean_gamma: empty weight matrix")
+    return np.float32(abs_sum_f64(W) / float(W.size))
+
+
+def absmean_gamma_fsum(W: np.ndarray) -> np.float32:
+    """Same definition via ``math.fsum`` (correctly rounded float64 sum); small inputs only."""
+    W = np.asarray(W, dtype=np.float32)
+    vals = np.abs(W.astype(np.float64)).ravel().tolist()
+    return np.float32(math.fsum(vals) / float(W.size))
+
+
+# ---------------------------------------------------------------------------
+# a2: RoundClip ternarisation and 2-bit packing  [PMV §1 RoundClip, §3 2-bit pack]
+# ---------------------------------------------------------------------------
+
+def ternary_codes(W: np.ndarray, gamma) -> np.ndarray:
+    """W_q = Round(Clip(W / (gamma + eps), -1, 1)) in {-1, 0, +1}  [PMV §1].
+
+    float32 throughout: d = fp32(gamma + eps), t = fp32(W / d) (IEEE division),
+    clip to [-1, 1], round half to even.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    d = np.float32(np.float32(gamma) + EPS32)
+    t = W / d
+    assert t.dtype == np.float32
+    c = np.clip(t, np.float32(-1.0), np.float32(1.0))
+    return np.rint(c).astype(np.int8)
+
+
+def padded_k(K: int) -> int:
+    return ((K + PAD_MULTIPLE - 1) // PAD_MULTIPLE) * PAD_MULTIPLE
+
+
+def pack_codes(q: np.ndarray) -> np.ndarray:
+    """Pack ternary codes [N, K] into uint32 words [N, padded_k(K) // 16].
+
+    Layout: see the module docstring.  0.25 byte per weight  [PMV §3].
+    """
+    q = np.asarray(q)
+    N, K = q.shape
+    Kp = padded_k(K)
+    c = np.ones((N, Kp), dtype=np.uint32)
+    c[:, :K] = (q.astype(np.int64) + 1).astype(np.uint32)
+    c = c.reshape(N, Kp // 16, 4, 4)  # [n, word j, i, b] -> k = 16j + 4i + b
+    words = np.zeros((N, Kp // 16), dtype=np.uint32)
+    for i in range(4):
+        for b in range(4):
+            words |= c[:, :, i, b] << np.uint32(8 * b + 2 * i)
+    return words
+
+
+def unpack_codes(words: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of :func:`pack_codes`; returns int8 codes [N, K] (raises on field value 3)."""
+    words = np.asarray(words, dtype=np.uint32)
+    N, nw = words.shape
+    out = np.empty((N, nw, 4, 4), dtype=np.int64)
+    for i in range(4):
+        for b in range(4):
+            out[:, :, i, b] = (words >> np.uint32(8 * b + 2 * i)) & np.uint32(3)
+    if np.any(out == 3):
+        raise ValueError("unpack_codes: invalid 2-bit field (3)")
+    return (out.reshape(N, nw * 16)[:, :K] - 1).astype(np.int8)
+
+
+# ---------------------------------------------------------------------------
+# a3: per-token AbsMax INT8  [PMV §1, AbsMax equations]
+# ---------------------------------------------------------------------------
+
+def absmax_quantize(X: np.ndarray):
+    """gamma_A = max_k |A_k| per token; A_q = Clip(Round(A * (127 / (gamma_A + eps))), -128, 127).
+
+    Returns (gamma_A float32 [M], Xq int8 [M, K], rowsum int64 [M]) where rowsum
+    is the exact sum of each token's codes.  float32 arithmetic, true division,
+    round half to even.
+    """
+    X = np.asarray(X, dtype=np.float32)
+    gA = np.max(np.abs(X), axis=1).astype(np.float32)
+    den = (gA + EPS32).astype(np.float32)
+    s = (np.float32(127.0) / den).astype(np.float32)
+    v = X * s[:, None]
+    assert v.dtype == np.float32
+    Xq = np.clip(np.rint(v), -128, 127).astype(np.int8)
+    return gA, Xq, Xq.astype(np.int64).sum(axis=1)
+
+
+# ---------------------------------------------------------------------------
+# a4/a5: Zero-GEMM contraction with INT32 accumulation  [PMV §2]
+# ---------------------------------------------------------------------------
+
+def zero_gemm_dot(xq, q) -> int:
+    """One output, literally as the article's Zero-GEMM: +1 adds, -1 subtracts, 0 skips."""
+    acc = 0
+    for a, w in zip(xq, q):
+        w = int(w)
+        if w == 1:
+            acc += int(a)
+        elif w == -1:
+            acc -= int(a)
+        elif w != 0:
+            raise ValueError("zero_gemm_dot: weight not ternary")
+    if not -(1 << 31) <= acc < (1 << 31):
+        raise OverflowError("zero_gemm_dot: INT32 accumulator overflow")
+    return acc
+
+
+def zero_gemm_naive(Xq: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """acc[m, n] = zero_gemm_dot(Xq[m], q[n]) for every pair (small inputs only)."""
+    M, N = Xq.shape[0], q.shape[0]
+    acc = np.empty((M, N), dtype=np.int64)
+    for m in range(M):
+        xr = Xq[m].tolist()
+        for n in range(N):
+            acc[m, n] = zero_gemm_dot(xr, q[n].tolist())
+    return acc
+
+
+def zero_gemm(Xq: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """acc = A_q x W_q^T as exact integers, via a float64 matrix product.
+
+    Every partial sum is an integer of magnitude <= 128 * K < 2**53, so the
+    float64 product is exact whatever order the library sums in.
+    """
+    Xq = np.asarray(Xq)
+    q = np.asarray(q)
+    K = Xq.shape[1]
+    if 128 * K >= (1 << 53):
+        raise ValueError("zero_gemm: K too large for an exact float64 contraction")
+    acc = Xq.astype(np.float64) @ q.astype(np.float64).T
+    return acc.astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
+# a6: dequantisation  [PMV §2, rescale by gamma_A * gamma / 127]
+# ---------------------------------------------------------------------------
+
+def dequant(acc: np.ndarray, gamma, gamma_a: np.ndarray) -> np.ndarray:
+    """Y[m, n] = acc[m, n] * gamma * gamma_A[m] / 127, formed in float64, rounded once to float32."""
+    acc = np.asarray(acc, dtype=np.float64)
+    g = float(np.float32(gamma))
+    ga = np.asarray(gamma_a, dtype=np.float32).astype(np.float64)
+    return (acc * g * ga[:, None] / 127.0).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Whole forward
+# ---------------------------------------------------------------------------
+
+def quantize_weights(W: np.ndarray):
+    """Offline half of BitLinear: (gamma, codes, packed words)."""
+    gamma = absmean_gamma(W)
+    q = ternary_codes(W, gamma)
+    return gamma, q, pack_codes(q)
+
+
+def bitlinear_forward(X: np.ndarray, W: np.ndarray) -> Dict[str, np.ndarray]:
+    """Full BitLinear forward Y = dequant(A_q x W_q^T); returns every intermediate."""
+    gamma, q, packed = quantize_weights(W)
+    gA, Xq, rowsum = absmax_quantize(X)
+    acc = zero_gemm(Xq, q)
+    Y = dequant(acc, gamma, gA)
+    return {"gamma": gamma, "q": q, "packed": packed, "gamma_a": gA, "Xq": Xq,
+            "rowsum": rowsum, "acc": acc, "Y": Y}
+
+
+def forward_from_codes(X: np.ndarray, q: np.ndarray, gamma) -> Dict[str, np.ndarray]:
+    """Forward for already-ternarised weights (codes + gamma)."""
+    gA, Xq, rowsum = absmax_quantize(X)
+    acc = zero_gemm(Xq, q)
+    return {"gamma_a": gA, "Xq": Xq, "rowsum": rowsum, "acc": acc,
+            "Y": dequant(acc, gamma, gA)}
+
+
+def sampled_forward(X: np.ndarray, q: np.ndarray, gamma, rows, cols) -> Dict[str, np.ndarray]:
+    """Outputs for a subset of tokens (rows) and output channels (cols) only.
+
+    Each token's quantisation depends only on that token, and each output only
+    on one token and one weight row, so a sample is computed exactly as the
+    full forward would compute it.
+    """
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    gA, Xq, rowsum = absmax_quantize(np.asarray(X)[rows])
+    acc = zero_gemm(Xq, np.asarray(q)[cols])
+    return {"gamma_a": gA, "Xq": Xq, "rowsum": rowsum, "acc": acc,
+            "Y": dequant(acc, gamma, gA)}
