@@ -1,0 +1,181 @@
+"""BitNet b1.58 BitLinear forward on MI355X (gfx950).
+
+A thin torch-facing binding over the C ABI in ``include/bitlinear.h``: these
+functions only check and marshal arguments (device pointers, sizes, the
+current HIP stream); every step of the computation runs in the HIP kernels of
+``libbitlinear.so``.  There is no CPU fallback: without the built library or a
+GPU the calls raise.
+
+    packed, gamma = quantize_weights(W)           # W: float32 [N, K] on the GPU
+    Y = forward(X, packed, gamma, K)              # X: float32/bfloat16 [M, K] -> float32 [M, N]
+"""
+from __future__ import annotations
+
+from . import abi
+from .abi import BitLinearError
+
+__all__ = [
+    "BitLinearError",
+    "padded_k",
+    "packed_words",
+    "quantize_weights",
+    "quantize_activations",
+    "forward",
+    "forward_batched",
+    "max_decode_m",
+    "decode_fits",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes_void(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def ctypes_void(v):
+    import ctypes
+    return ctypes.c_void_p(v)
+
+
+def _ptr(t):
+    import ctypes
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require_cuda(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def padded_k(K: int) -> int:
+    return int(abi.load().bitlinear_padded_k(K))
+
+
+def packed_words(K: int) -> int:
+    """uint32 words per packed row."""
+    return padded_k(K) // 16
+
+
+def max_decode_m() -> int:
+    return int(abi.load().bitlinear_max_decode_m())
+
+
+def decode_fits(M: int, K: int) -> bool:
+    lib = abi.load()
+    return M <= lib.bitlinear_max_decode_m() and M * (padded_k(K) + 16) <= lib.bitlinear_max_decode_codes()
+
+
+def _x_dtype(X):
+    torch = _torch()
+    if X.dtype == torch.float32:
+        return abi.F32
+    if X.dtype == torch.bfloat16:
+        return abi.BF16
+    raise ValueError("X must be float32 or bfloat16")
+
+
+def quantize_weights(W):
+    """AbsMean ternarisation + 2-bit packing of a float32 [N, K] GPU tensor.
+
+    Returns (packed int32 [N, padded_k(K) // 16] holding uint32 words, gamma float32 [1]).
+    """
+    torch = _torch()
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a float32 [N, K] tensor")
+    lib = abi.load()
+    N, K = W.shape
+    packed = torch.empty((N, packed_words(K)), dtype=torch.int32, device=W.device)
+    gamma = torch.empty((1,), dtype=torch.float32, device=W.device)
+    ws_bytes = lib.bitlinear_quantize_workspace_bytes()
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
+    abi.check("bitlinear_quantize_weights",
+              lib.bitlinear_quantize_weights(_ptr(W), N, K, _ptr(packed), _ptr(gamma), _ptr(ws),
+                                             ws_bytes, _stream(W)))
+    return packed, gamma
+
+
+def quantize_activations(X):
+    """Per-token AbsMax INT8 codes: (Xq int8 [M, padded_k(K)], gamma_a float32 [M], rowsum int32 [M])."""
+    torch = _torch()
+    _require_cuda(X, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    lib = abi.load()
+    M, K = X.shape
+    Xq = torch.empty((M, padded_k(K)), dtype=torch.int8, device=X.device)
+    ga = torch.empty((M,), dtype=torch.float32, device=X.device)
+    rs = torch.empty((M,), dtype=torch.int32, device=X.device)
+    abi.check("bitlinear_quantize_activations",
+              lib.bitlinear_quantize_activations(_ptr(X), _x_dtype(X), M, K, _ptr(Xq), _ptr(ga),
+                                                 _ptr(rs), _stream(X)))
+    return Xq, ga, rs
+
+
+_PATHS = {"auto": abi.PATH_AUTO, "decode": abi.PATH_DECODE, "prefill": abi.PATH_PREFILL}
+
+
+def forward(X, packed, gamma, K: int | None = None, path: str = "auto", return_acc: bool = False,
+            out=None, workspace=None):
+    """Y = dequant(A_q x W_q^T) for X [M, K] (float32 or bfloat16) -> float32 [M, N].
+
+    ``path`` forces the decode or prefill kernels; ``return_acc`` also returns
+    the exact INT32 accumulator [M, N].
+    """
+    torch = _torch()
+    _require_cuda(X, "X")
+    _require_cuda(packed, "packed")
+    _require_cuda(gamma, "gamma")
+    if X.dim() != 2 or packed.dim() != 2:
+        raise ValueError("X must be [M, K] and packed [N, words]")
+    M, Kx = X.shape
+    K = Kx if K is None else K
+    if K != Kx:
+        raise ValueError("K does not match X")
+    N = packed.shape[0]
+    if packed.shape[1] != packed_words(K) or packed.element_size() != 4:
+        raise ValueError("packed does not hold padded_k(K) // 16 32-bit words per row")
+    lib = abi.load()
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=X.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=X.device) if return_acc else None
+    ws_bytes = 0
+    ws = workspace
+    if ws is None and not (path == "decode" or (path == "auto" and decode_fits(M, K))):
+        ws_bytes = lib.bitlinear_forward_workspace_bytes(M, K)
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=X.device)
+    elif ws is not None:
+        ws_bytes = ws.numel() * ws.element_size()
+    abi.check("bitlinear_forward_ex",
+              lib.bitlinear_forward_ex(_ptr(X), _x_dtype(X), M, K, _ptr(packed), N, _ptr(gamma),
+                                       _ptr(Y), _ptr(acc), _PATHS[path], _ptr(ws), ws_bytes,
+                                       _stream(X)))
+    return (Y, acc) if return_acc else Y
+
+
+def forward_batched(X, packed, gamma, K: int | None = None, out=None):
+    """L decode forwards in one launch: X [L, M, K], packed [L, N, words], gamma [L] -> Y [L, M, N]."""
+    torch = _torch()
+    for t, nm in ((X, "X"), (packed, "packed"), (gamma, "gamma")):
+        _require_cuda(t, nm)
+    if X.dim() != 3 or packed.dim() != 3:
+        raise ValueError("X must be [L, M, K] and packed [L, N, words]")
+    L, M, Kx = X.shape
+    K = Kx if K is None else K
+    if K != Kx or packed.shape[0] != L or gamma.numel() != L:
+        raise ValueError("inconsistent batched shapes")
+    N = packed.shape[1]
+    if packed.shape[2] != packed_words(K):
+        raise ValueError("packed does not hold padded_k(K) // 16 words per row")
+    lib = abi.load()
+    Y = out if out is not None else torch.empty((L, M, N), dtype=torch.float32, device=X.device)
+    abi.check("bitlinear_forward_batched",
+              lib.bitlinear_forward_batched(L, _ptr(X), _x_dtype(X), M, K, _ptr(packed), N,
+                                            _ptr(gamma), _ptr(Y), _stream(X)))
+    return Y

@@ -1,0 +1,82 @@
+"""ctypes view of libbitlinear.so: the C ABI declared in include/bitlinear.h.
+
+Loading is lazy and fails loudly: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+OK = 0
+ERR_NULL = -1
+ERR_SHAPE = -2
+ERR_DTYPE = -3
+ERR_ALIGN = -4
+ERR_WORKSPACE = -5
+ERR_HIP = -6
+ERR_ARG = -7
+
+F32 = 0
+BF16 = 1
+
+PATH_AUTO = 0
+PATH_DECODE = 1
+PATH_PREFILL = 2
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+_p = ctypes.c_void_p
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "bitlinear_padded_k": (_i64, [_i64]),
+    "bitlinear_packed_bytes": (_sz, [_i64, _i64]),
+    "bitlinear_quantize_workspace_bytes": (_sz, []),
+    "bitlinear_forward_workspace_bytes": (_sz, [_i64, _i64]),
+    "bitlinear_max_decode_m": (_int, []),
+    "bitlinear_max_decode_codes": (_i64, []),
+    "bitlinear_quantize_weights": (_int, [_p, _i64, _i64, _p, _p, _p, _sz, _p]),
+    "bitlinear_quantize_activations": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p]),
+    "bitlinear_forward": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _sz, _p]),
+    "bitlinear_forward_ex": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _int, _p, _sz, _p]),
+    "bitlinear_forward_batched": (_int, [_i64, _p, _int, _i64, _i64, _p, _i64, _p, _p, _p]),
+    "bitlinear_status_string": (ctypes.c_char_p, [_int]),
+}
+
+_LIB = None
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m bitlinear_absmean_ternarise_bit_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().bitlinear_status_string(status).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != OK:
+        raise BitLinearError(fn, status)

@@ -1,0 +1,171 @@
+// C ABI of the BitLinear library: argument checks, path choice, launches.
+// Every check runs on the host before anything is enqueued.
+#include <stdint.h>
+
+#include "../../include/bitlinear.h"
+#include "kernels.hpp"
+
+using namespace bitlinear;
+
+namespace {
+
+constexpr int64_t kMaxK = int64_t(1) << 20;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_mnk(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return BITLINEAR_ERR_SHAPE;
+  if (K > kMaxK) return BITLINEAR_ERR_SHAPE;
+  if (N > (int64_t(1) << 31) || M > (int64_t(1) << 31)) return BITLINEAR_ERR_SHAPE;
+  if (static_cast<uint64_t>(N) * static_cast<uint64_t>(K) >= (uint64_t(1) << 32)) return BITLINEAR_ERR_SHAPE;
+  if (static_cast<uint64_t>(M) * static_cast<uint64_t>(N) >= (uint64_t(1) << 40)) return BITLINEAR_ERR_SHAPE;
+  if (static_cast<uint64_t>(M) * static_cast<uint64_t>(K) >= (uint64_t(1) << 40)) return BITLINEAR_ERR_SHAPE;
+  return BITLINEAR_OK;
+}
+
+int check_x(const void* X, int x_dtype) {
+  if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16) return BITLINEAR_ERR_DTYPE;
+  if (!aligned(X, x_dtype == BITLINEAR_F32 ? 4 : 2)) return BITLINEAR_ERR_ALIGN;
+  return BITLINEAR_OK;
+}
+
+bool decode_fits(int64_t M, int64_t K) {
+  return M <= kDecodeMaxM && M * (padded_k(K) + 16) <= kDecodeMaxCodes;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct PrefillWs {
+  int8_t* xq;
+  float* ga;
+  int32_t* rs;
+};
+
+size_t prefill_ws_bytes(int64_t M, int64_t K) {
+  return align256(static_cast<size_t>(M) * static_cast<size_t>(padded_k(K))) +
+         align256(static_cast<size_t>(M) * 4) + align256(static_cast<size_t>(M) * 4);
+}
+
+PrefillWs prefill_ws(void* ws, int64_t M, int64_t K) {
+  char* p = static_cast<char*>(ws);
+  PrefillWs w;
+  w.xq = reinterpret_cast<int8_t*>(p);
+  p += align256(static_cast<size_t>(M) * static_cast<size_t>(padded_k(K)));
+  w.ga = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(M) * 4);
+  w.rs = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BITLINEAR_OK : BITLINEAR_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t bitlinear_padded_k(int64_t K) { return K < 1 ? 0 : padded_k(K); }
+
+size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(padded_k(K)) / 4;
+}
+
+size_t bitlinear_quantize_workspace_bytes(void) { return quantize_workspace_bytes(); }
+
+size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < 1) return 0;
+  return prefill_ws_bytes(M, K);
+}
+
+int bitlinear_max_decode_m(void) { return kDecodeMaxM; }
+
+int64_t bitlinear_max_decode_codes(void) { return kDecodeMaxCodes; }
+
+int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint32_t* packed, float* gamma,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!W || !packed || !gamma) return BITLINEAR_ERR_NULL;
+  int st = check_mnk(1, N, K);
+  if (st) return st;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(gamma, 4)) return BITLINEAR_ERR_ALIGN;
+  if (!workspace || workspace_bytes < quantize_workspace_bytes()) return BITLINEAR_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return BITLINEAR_ERR_ALIGN;
+  return hip_status(launch_quantize_weights(W, N, K, packed, gamma, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_quantize_activations(const void* X, int x_dtype, int64_t M, int64_t K, int8_t* Xq,
+                                   float* gamma_a, int32_t* rowsum, void* stream) {
+  if (!X || !Xq || !gamma_a || !rowsum) return BITLINEAR_ERR_NULL;
+  int st = check_mnk(M, 1, K);
+  if (st) return st;
+  st = check_x(X, x_dtype);
+  if (st) return st;
+  if (!aligned(Xq, 16) || !aligned(gamma_a, 4) || !aligned(rowsum, 4)) return BITLINEAR_ERR_ALIGN;
+  return hip_status(launch_act_quant(X, x_dtype, M, K, Xq, gamma_a, rowsum,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward_ex(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
+                         int64_t N, const float* gamma, float* Y, int32_t* acc, int path,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!X || !packed || !gamma || !Y) return BITLINEAR_ERR_NULL;
+  int st = check_mnk(M, N, K);
+  if (st) return st;
+  st = check_x(X, x_dtype);
+  if (st) return st;
+  if (path != BITLINEAR_PATH_AUTO && path != BITLINEAR_PATH_DECODE && path != BITLINEAR_PATH_PREFILL)
+    return BITLINEAR_ERR_ARG;
+  if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(Y, 4) || (acc && !aligned(acc, 4)))
+    return BITLINEAR_ERR_ALIGN;
+  const bool fits = decode_fits(M, K);
+  if (path == BITLINEAR_PATH_DECODE && !fits) return BITLINEAR_ERR_SHAPE;
+  const bool decode = path == BITLINEAR_PATH_DECODE || (path == BITLINEAR_PATH_AUTO && fits);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (decode) return hip_status(launch_decode(X, x_dtype, M, K, packed, N, gamma, Y, acc, 1, s));
+  if (!workspace || workspace_bytes < prefill_ws_bytes(M, K)) return BITLINEAR_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITLINEAR_ERR_ALIGN;
+  PrefillWs w = prefill_ws(workspace, M, K);
+  hipError_t e = launch_act_quant(X, x_dtype, M, K, w.xq, w.ga, w.rs, s);
+  if (e != hipSuccess) return BITLINEAR_ERR_HIP;
+  return hip_status(launch_prefill_gemm(w.xq, w.ga, w.rs, M, K, packed, N, gamma, Y, acc, s));
+}
+
+int bitlinear_forward(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
+                      int64_t N, const float* gamma, float* Y, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return bitlinear_forward_ex(X, x_dtype, M, K, packed, N, gamma, Y, nullptr, BITLINEAR_PATH_AUTO,
+                              workspace, workspace_bytes, stream);
+}
+
+int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, int64_t K,
+                              const uint32_t* packed, int64_t N, const float* gamma, float* Y,
+                              void* stream) {
+  if (!X || !packed || !gamma || !Y) return BITLINEAR_ERR_NULL;
+  if (L < 1 || L > (int64_t(1) << 20)) return BITLINEAR_ERR_SHAPE;
+  int st = check_mnk(M, N, K);
+  if (st) return st;
+  st = check_x(X, x_dtype);
+  if (st) return st;
+  if (!decode_fits(M, K)) return BITLINEAR_ERR_SHAPE;
+  const int64_t bpl = (N + 63) / 64;
+  if (L * bpl >= (int64_t(1) << 31)) return BITLINEAR_ERR_SHAPE;
+  if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(Y, 4)) return BITLINEAR_ERR_ALIGN;
+  return hip_status(launch_decode(X, x_dtype, M, K, packed, N, gamma, Y, nullptr, L,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+const char* bitlinear_status_string(int status) {
+  switch (status) {
+    case BITLINEAR_OK: return "ok";
+    case BITLINEAR_ERR_NULL: return "a required pointer is NULL";
+    case BITLINEAR_ERR_SHAPE: return "M, N, K or L out of the supported range";
+    case BITLINEAR_ERR_DTYPE: return "unknown activation dtype";
+    case BITLINEAR_ERR_ALIGN: return "a pointer is not aligned as required";
+    case BITLINEAR_ERR_WORKSPACE: return "workspace missing or too small";
+    case BITLINEAR_ERR_HIP: return "a HIP call or kernel launch failed";
+    case BITLINEAR_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Shared device helpers for the BitLinear kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitlinear {
+
+constexpr int kWave = 64;
+constexpr float kEps = 1e-5f;  // eps of both quantisers, a float32 constant
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ unsigned wave_or(unsigned v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// bfloat16 bit pattern -> float32 (exact widening)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Four 2-bit codes per byte lane: (word >> 2i) & 0x03030303 gives the int8
+// codes of k = 16j + 4i .. 16j + 4i + 3, so the four results are the sixteen
+// codes of a packed word in k order.
+__device__ __forceinline__ v4i unpack_word(uint32_t w) {
+  v4i r;
+  r[0] = static_cast<int>(w & 0x03030303u);
+  r[1] = static_cast<int>((w >> 2) & 0x03030303u);
+  r[2] = static_cast<int>((w >> 4) & 0x03030303u);
+  r[3] = static_cast<int>((w >> 6) & 0x03030303u);
+  return r;
+}
+
+// Activation code of one value: rint(x * s) (half to even) clipped to [-128, 127].
+__device__ __forceinline__ int act_code(float x, float s) {
+  float v = __fmul_rn(x, s);
+  float r = __builtin_rintf(v);
+  r = fminf(fmaxf(r, -128.0f), 127.0f);
+  return static_cast<int>(r);
+}
+
+}  // namespace bitlinear

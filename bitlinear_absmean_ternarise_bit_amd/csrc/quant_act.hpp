@@ -1,0 +1,110 @@
+// Per-token AbsMax INT8 quantisation of one activation row by one wavefront.
+//
+// [PMV] = produtoramaxvision.com.br article on BitNet b1.58; its section-1
+// AbsMax equations: gamma_A = max_k |A_k| per token and
+// A_q = Clip(Round(A * (127 / (gamma_A + eps))), -128, 127).
+//
+// Float32 arithmetic: one IEEE division per token for the scale, then
+// rint(x * s) (half to even).  The max and the code sum are exact, so the
+// wave reductions' order does not matter.
+#pragma once
+
+#include "common.hpp"
+
+namespace bitlinear {
+
+// DT: 0 = float32, 1 = bfloat16.  VEC: rows are 16-byte aligned and hold a
+// whole number of 16-byte chunks.
+template <int DT>
+struct ActTraits;
+template <>
+struct ActTraits<0> {
+  static constexpr int kPerChunk = 4;  // float32 values per 16 bytes
+};
+template <>
+struct ActTraits<1> {
+  static constexpr int kPerChunk = 8;  // bfloat16 values per 16 bytes
+};
+
+template <int DT>
+__device__ __forceinline__ void chunk_to_f32(const uint4 v, float* f) {
+  if constexpr (DT == 0) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  } else {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float load_one(const void* row, int64_t k) {
+  if constexpr (DT == 0) return static_cast<const float*>(row)[k];
+  else return bf16_to_f32(static_cast<const uint16_t*>(row)[k]);
+}
+
+// Quantise row `row` (K values) into dst[0..Kp) (zeros in [K, Kp)); every lane
+// of the wave must call it.  Returns gamma_A and the code sum in all lanes.
+template <int DT, bool VEC>
+__device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, int64_t K, int64_t Kp,
+                                                  int lane, int8_t* __restrict__ dst,
+                                                  float& gamma_a, int& codesum) {
+  constexpr int P = ActTraits<DT>::kPerChunk;
+  float mx = 0.0f;
+  if constexpr (VEC) {
+    const uint4* r4 = static_cast<const uint4*>(row);
+    const int64_t nc = K / P;
+    for (int64_t c = lane; c < nc; c += kWave) {
+      float f[P];
+      chunk_to_f32<DT>(r4[c], f);
+#pragma unroll
+      for (int i = 0; i < P; ++i) mx = fmaxf(mx, fabsf(f[i]));
+    }
+  } else {
+    for (int64_t k = lane; k < K; k += kWave) mx = fmaxf(mx, fabsf(load_one<DT>(row, k)));
+  }
+  mx = wave_max(mx);
+  const float s = __fdiv_rn(127.0f, __fadd_rn(mx, kEps));
+
+  int sum = 0;
+  if constexpr (VEC) {
+    const uint4* r4 = static_cast<const uint4*>(row);
+    const int64_t nc = K / P;
+    for (int64_t c = lane; c < nc; c += kWave) {
+      float f[P];
+      chunk_to_f32<DT>(r4[c], f);
+      uint32_t w[P / 4];
+#pragma unroll
+      for (int q = 0; q < P / 4; ++q) {
+        uint32_t packedq = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int code = act_code(f[4 * q + b], s);
+          sum += code;
+          packedq |= (static_cast<uint32_t>(code) & 0xffu) << (8 * b);
+        }
+        w[q] = packedq;
+      }
+      if constexpr (P == 8) {
+        *reinterpret_cast<uint2*>(dst + c * P) = make_uint2(w[0], w[1]);
+      } else {
+        *reinterpret_cast<uint32_t*>(dst + c * P) = w[0];
+      }
+    }
+  } else {
+    for (int64_t k = lane; k < K; k += kWave) {
+      const int code = act_code(load_one<DT>(row, k), s);
+      sum += code;
+      dst[k] = static_cast<int8_t>(code);
+    }
+  }
+  for (int64_t k = K + lane; k < Kp; k += kWave) dst[k] = 0;
+  gamma_a = mx;
+  codesum = wave_sum(sum);
+}
+
+}  // namespace bitlinear

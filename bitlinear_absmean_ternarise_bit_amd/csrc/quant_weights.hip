@@ -1,0 +1,236 @@
+// Offline weight quantisation: AbsMean scale, RoundClip ternary codes, 2-bit pack.
+//
+// [PMV] = produtoramaxvision.com.br article on BitNet b1.58 (ternary
+// quantisation, BitLinear, Zero-GEMM).  gamma = (1/(n m)) sum |W_ij| and
+// W_q = Round(Clip(W / (gamma + eps), -1, 1)) are its section-1 AbsMean
+// equations; 2 bits per weight is its section-3 packing.
+//
+// gamma is computed exactly and order-independently: each |w| is an integer
+// significand times a power of two, so the sum is an integer in units of
+// 2^-149.  Lanes accumulate it as base-2^32 "digits" held carry-save in
+// uint64 registers (a value lands in two adjacent digits); one block-wide
+// table of ten digits per workgroup goes to the workspace, and a single
+// workgroup adds the tables, propagates carries, rounds the exact sum once to
+// float64 and divides by N*K.  Any grid shape gives bit-identical results.
+#include "kernels.hpp"
+
+namespace bitlinear {
+
+namespace {
+
+constexpr int kDigits = 10;
+
+struct DigitAcc {
+  unsigned long long a0 = 0, a1 = 0, a2 = 0;  // digits T0, T0+1, T0+2
+};
+
+// Split |w| (float32 bit pattern) into (digit index t, low 32 bits, high bits)
+// of sig << r, where |w| = sig * 2^(32 t + r) * 2^-149.
+__device__ __forceinline__ void split_abs(uint32_t bits, uint32_t& t, uint32_t& lo, uint32_t& hi) {
+  const uint32_t b = bits & 0x7fffffffu;
+  const uint32_t e = b >> 23;
+  const uint32_t m = b & 0x7fffffu;
+  const uint32_t sig = e ? (m | 0x800000u) : m;
+  const uint32_t s = e ? e - 1u : 0u;
+  t = s >> 5;
+  const uint64_t v = static_cast<uint64_t>(sig) << (s & 31u);
+  lo = static_cast<uint32_t>(v);
+  hi = static_cast<uint32_t>(v >> 32);
+}
+
+__device__ __forceinline__ void add_abs(uint32_t bits, uint32_t T0, DigitAcc& acc,
+                                        unsigned long long* sdig) {
+  uint32_t t, lo, hi;
+  split_abs(bits, t, lo, hi);
+  if (t == T0) {
+    acc.a0 += lo;
+    acc.a1 += hi;
+  } else if (t == T0 + 1u) {
+    acc.a1 += lo;
+    acc.a2 += hi;
+  } else if (lo | hi) {  // outside the wave's window (rare): block table
+    atomicAdd(&sdig[t], static_cast<unsigned long long>(lo));
+    atomicAdd(&sdig[t + 1], static_cast<unsigned long long>(hi));
+  }
+}
+
+__global__ __launch_bounds__(256) void absmean_digits_kernel(const float* __restrict__ W,
+                                                             uint64_t n,
+                                                             unsigned long long* __restrict__ partial) {
+  __shared__ unsigned long long sdig[kDigits];
+  if (threadIdx.x < kDigits) sdig[threadIdx.x] = 0;
+  __syncthreads();
+
+  const uint64_t n4 = n >> 2;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  const uint64_t tid = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const uint4* W4 = reinterpret_cast<const uint4*>(W);
+
+  // Window base: one digit below the largest digit among the wave's first
+  // loads (any choice is exact; this one keeps nearly every value in-window).
+  uint4 first = make_uint4(0, 0, 0, 0);
+  if (tid < n4) first = W4[tid];
+  uint32_t tmax = 0;
+  {
+    uint32_t t, lo, hi;
+    split_abs(first.x, t, lo, hi); tmax = max(tmax, (lo | hi) ? t : 0u);
+    split_abs(first.y, t, lo, hi); tmax = max(tmax, (lo | hi) ? t : 0u);
+    split_abs(first.z, t, lo, hi); tmax = max(tmax, (lo | hi) ? t : 0u);
+    split_abs(first.w, t, lo, hi); tmax = max(tmax, (lo | hi) ? t : 0u);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tmax = max(tmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmax), o, kWave)));
+  const uint32_t T0 = tmax ? tmax - 1u : 0u;
+
+  DigitAcc acc;
+  if (tid < n4) {
+    add_abs(first.x, T0, acc, sdig);
+    add_abs(first.y, T0, acc, sdig);
+    add_abs(first.z, T0, acc, sdig);
+    add_abs(first.w, T0, acc, sdig);
+  }
+  for (uint64_t i = tid + stride; i < n4; i += stride) {
+    const uint4 v = W4[i];
+    add_abs(v.x, T0, acc, sdig);
+    add_abs(v.y, T0, acc, sdig);
+    add_abs(v.z, T0, acc, sdig);
+    add_abs(v.w, T0, acc, sdig);
+  }
+  // scalar tail (n not a multiple of 4)
+  const uint64_t tail = n4 << 2;
+  if (tid < n - tail) add_abs(__float_as_uint(W[tail + tid]), T0, acc, sdig);
+
+  const unsigned long long s0 = wave_sum_u64(acc.a0);
+  const unsigned long long s1 = wave_sum_u64(acc.a1);
+  const unsigned long long s2 = wave_sum_u64(acc.a2);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    if (s0) atomicAdd(&sdig[T0], s0);
+    if (s1) atomicAdd(&sdig[T0 + 1], s1);
+    if (s2) atomicAdd(&sdig[T0 + 2], s2);
+  }
+  __syncthreads();
+  if (threadIdx.x < kDigits) partial[static_cast<uint64_t>(blockIdx.x) * kDigits + threadIdx.x] = sdig[threadIdx.x];
+}
+
+// Sum the per-workgroup digit tables, round the exact sum to float64 once,
+// gamma = float32(sum / count).
+__global__ __launch_bounds__(256) void absmean_finalize_kernel(const unsigned long long* __restrict__ partial,
+                                                               int nparts, double count,
+                                                               float* __restrict__ gamma) {
+  __shared__ unsigned long long red[kDigits][256 / kWave];
+  unsigned long long d[kDigits];
+#pragma unroll
+  for (int i = 0; i < kDigits; ++i) d[i] = 0;
+  for (int p = threadIdx.x; p < nparts; p += blockDim.x) {
+#pragma unroll
+    for (int i = 0; i < kDigits; ++i) d[i] += partial[static_cast<uint64_t>(p) * kDigits + i];
+  }
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int i = 0; i < kDigits; ++i) {
+    const unsigned long long s = wave_sum_u64(d[i]);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[i][wave] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+
+  // carry-propagate into 32-bit limbs: S = sum_i limb[i] * 2^(32 i)
+  uint32_t limb[kDigits + 2];
+  unsigned long long carry = 0;
+#pragma unroll
+  for (int i = 0; i < kDigits; ++i) {
+    unsigned long long v = carry;
+    for (int w = 0; w < 256 / kWave; ++w) v += red[i][w];  // < 2^64 for N*K < 2^32
+    limb[i] = static_cast<uint32_t>(v);
+    carry = v >> 32;
+  }
+  limb[kDigits] = static_cast<uint32_t>(carry);
+  limb[kDigits + 1] = static_cast<uint32_t>(carry >> 32);
+
+  int top = kDigits + 1;
+  while (top >= 0 && limb[top] == 0) --top;
+  double sum = 0.0;
+  if (top >= 0) {
+    // top 64 significant bits T, exponent so that S ~= T * 2^(32 top - 32 - lz)
+    const int lz = __clz(limb[top]);
+    const uint64_t h = (static_cast<uint64_t>(limb[top]) << 32) | (top >= 1 ? limb[top - 1] : 0u);
+    const uint64_t l = static_cast<uint64_t>(top >= 2 ? limb[top - 2] : 0u) << 32;
+    uint64_t T = lz ? ((h << lz) | (l >> (64 - lz))) : h;
+    bool sticky = lz ? ((l << lz) != 0) : (l != 0);
+    for (int i = top - 3; i >= 0; --i) sticky |= (limb[i] != 0);
+    if (sticky) T |= 1u;  // below the float64 round bit: decides ties correctly
+    // hi * 2^32 is exact and the one addition rounds once: correctly rounded
+    const double t = static_cast<double>(static_cast<uint32_t>(T >> 32)) * 4294967296.0 +
+                     static_cast<double>(static_cast<uint32_t>(T));
+    sum = ldexp(t, 32 * top - 32 - lz - 149);
+  }
+  gamma[0] = static_cast<float>(sum / count);
+}
+
+// Ternarise and pack.  Each lane turns four consecutive weights (k = 4f..4f+3)
+// into the four bytes' bit pair 2i of word f/4 (i = f%4); four adjacent lanes
+// OR their parts into one word.
+template <bool VEC>
+__global__ __launch_bounds__(256) void ternarise_pack_kernel(const float* __restrict__ W, int64_t N,
+                                                             int64_t K, int64_t Kp,
+                                                             const float* __restrict__ gamma,
+                                                             uint32_t* __restrict__ packed) {
+  const float d = __fadd_rn(gamma[0], kEps);
+  const int64_t quads_per_row = Kp >> 2;
+  const int64_t total = N * quads_per_row;  // a multiple of 16: groups of 4 lanes stay together
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t f = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; f < total; f += stride) {
+    const int64_t n = f / quads_per_row;
+    const int64_t kq = (f - n * quads_per_row) << 2;
+    const float* row = W + n * K;
+    float w[4];
+    if (VEC && kq + 3 < K) {
+      const float4 v = *reinterpret_cast<const float4*>(row + kq);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w[b] = (kq + b < K) ? row[kq + b] : 0.0f;
+    }
+    uint32_t part = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      uint32_t c = 1u;  // padding: zero weight
+      if (kq + b < K) {
+        const float t = __fdiv_rn(w[b], d);
+        const float q = __builtin_rintf(fminf(fmaxf(t, -1.0f), 1.0f));
+        c = static_cast<uint32_t>(static_cast<int>(q) + 1);
+      }
+      part |= c << (8 * b);
+    }
+    const int i = static_cast<int>(f & 3);
+    part <<= 2 * i;
+    part |= __shfl_xor(part, 1, 4);
+    part |= __shfl_xor(part, 2, 4);
+    if (i == 0) packed[f >> 2] = part;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_t* packed,
+                                   float* gamma, void* workspace, hipStream_t stream) {
+  const uint64_t n = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
+  auto* partial = static_cast<unsigned long long*>(workspace);
+  const uint64_t want = (n / 4 + 255) / 256;
+  const int blocks = static_cast<int>(want < 1 ? 1 : (want > kAbsmeanBlocks ? kAbsmeanBlocks : want));
+  absmean_digits_kernel<<<blocks, 256, 0, stream>>>(W, n, partial);
+  absmean_finalize_kernel<<<1, 256, 0, stream>>>(partial, blocks, static_cast<double>(n), gamma);
+  const int64_t Kp = padded_k(K);
+  const int64_t total = N * (Kp / 4);
+  int64_t pblocks = (total + 255) / 256;
+  if (pblocks > 65536) pblocks = 65536;
+  if ((K & 3) == 0)
+    ternarise_pack_kernel<true><<<static_cast<int>(pblocks), 256, 0, stream>>>(W, N, K, Kp, gamma, packed);
+  else
+    ternarise_pack_kernel<false><<<static_cast<int>(pblocks), 256, 0, stream>>>(W, N, K, Kp, gamma, packed);
+  return hipGetLastError();
+}
+
+size_t quantize_workspace_bytes() { return static_cast<size_t>(kAbsmeanBlocks) * kDigits * 8; }
+
+}  // namespace bitlinear

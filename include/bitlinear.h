@@ -1,0 +1,184 @@
+/*
+ * bitlinear.h -- C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear forward.
+ *
+ * Citations: [PMV] is the produtoramaxvision.com.br blog article on BitNet b1.58
+ * (ternary quantisation, the BitLinear layer and Zero-GEMM).  [PMV s1] is its
+ * section on why ternary weights carry 1.58 bits (AbsMean and AbsMax
+ * equations), [PMV s2] the section on how BitLinear removes multiplications
+ * (add/subtract/skip, INT32 accumulation, rescale by gamma_A * gamma / 127),
+ * [PMV s3] the section on the memory wall (2-bit packing, 0.25 byte/weight).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Array pointers are DEVICE pointers to contiguous row-major arrays that the
+ *    caller allocates and owns.  The library allocates nothing and keeps no
+ *    mutable global state; calls on different streams do not interact.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call only enqueues work on it: no host synchronisation, results are ready
+ *    when the stream reaches them.  Faults inside kernels surface at the
+ *    caller's next synchronisation of that stream.
+ *  - Every argument is checked on the host before anything is launched; a
+ *    failed check returns a negative status and enqueues nothing.  A failed
+ *    launch returns BITLINEAR_ERR_HIP.  Nothing throws or aborts.
+ *  - Sizes: 1 <= M, N, K; N*K < 2^32; M*N < 2^40; K <= 2^20.
+ *  - Non-finite inputs (inf/nan in W or X) give unspecified results.
+ *
+ * Packed ternary weights (the format of `packed` everywhere)
+ * ----------------------------------------------------------
+ * Each weight is stored as a 2-bit code c = q + 1 in {0,1,2} (3 never occurs),
+ * [PMV s3].  A row of K weights is padded to Kp = bitlinear_padded_k(K) (a
+ * multiple of 64) with c = 1, i.e. zero weights, and stored as Kp/16
+ * little-endian uint32 words; bits [8b+2i, 8b+2i+1] of word j hold the code of
+ * k = 16j + 4i + b.  So `(word >> 2i) & 0x03030303` is four int8 codes for
+ * k = 16j+4i .. 16j+4i+3.  Rows follow each other with no gap:
+ * packed is uint32[N][Kp/16], bitlinear_packed_bytes(N, K) bytes.  The buffer
+ * carries no header: a forward must be given the K it was packed with.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define BITLINEAR_OK             0
+#define BITLINEAR_ERR_NULL      -1 /* a required pointer is NULL                  */
+#define BITLINEAR_ERR_SHAPE     -2 /* M, N, K or L out of the supported range      */
+#define BITLINEAR_ERR_DTYPE     -3 /* unknown activation dtype                     */
+#define BITLINEAR_ERR_ALIGN     -4 /* a pointer is not aligned as required         */
+#define BITLINEAR_ERR_WORKSPACE -5 /* workspace missing or smaller than required   */
+#define BITLINEAR_ERR_HIP       -6 /* a HIP call or kernel launch failed           */
+#define BITLINEAR_ERR_ARG       -7 /* another argument (path selector) is invalid  */
+
+/* ---- activation dtypes (Y is always float32) --------------------------- */
+#define BITLINEAR_F32  0
+#define BITLINEAR_BF16 1
+
+/* ---- forward path selector (bitlinear_forward_ex) ----------------------- */
+#define BITLINEAR_PATH_AUTO    0 /* decode for M <= bitlinear_max_decode_m(), else prefill */
+#define BITLINEAR_PATH_DECODE  1 /* fused quantise + GEMV kernel (M <= bitlinear_max_decode_m()) */
+#define BITLINEAR_PATH_PREFILL 2 /* activation quantiser + INT8-MFMA GEMM */
+
+/* ---- sizes ------------------------------------------------------------- */
+
+/* Kp: K rounded up to a multiple of 64 (the packed row length in weights). */
+int64_t bitlinear_padded_k(int64_t K);
+
+/* Bytes of a packed [N, K] ternary matrix: N * Kp / 4.  [PMV s3] */
+size_t bitlinear_packed_bytes(int64_t N, int64_t K);
+
+/* Workspace bytes bitlinear_quantize_weights needs (a constant, < 128 KiB). */
+size_t bitlinear_quantize_workspace_bytes(void);
+
+/* Workspace bytes bitlinear_forward / _ex need for an M x K activation on the
+ * prefill path: M*Kp int8 codes + M float32 scales + M int32 code sums, each
+ * part 256-byte aligned.  The decode path needs none (it may be passed 0). */
+size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t K);
+
+/* Largest M the decode path accepts (16), and the largest M*(Kp+16) it
+ * accepts (the codes of all tokens live in on-chip memory, each token row
+ * padded by 16 bytes: 65536 bytes). */
+int bitlinear_max_decode_m(void);
+int64_t bitlinear_max_decode_codes(void);
+
+/* ---- a1 + a2: offline weight quantisation ------------------------------ */
+/*
+ * gamma = (1/(N*K)) * sum |W|                      [PMV s1, AbsMean equation]
+ * q     = Round(Clip(W / (gamma + eps), -1, 1))    [PMV s1, RoundClip]
+ * then packed 2 bits per weight                    [PMV s3]
+ *
+ * W:      device float32 [N, K] row-major, 16-byte aligned.
+ * packed: device, bitlinear_packed_bytes(N, K) bytes, 16-byte aligned (output).
+ * gamma:  device float32[1] (output).
+ * workspace: device, >= bitlinear_quantize_workspace_bytes(), 16-byte aligned;
+ *         scratch only, contents on entry do not matter.
+ *
+ * Arithmetic: the sum of |W| is formed exactly (per-exponent integer digits)
+ * and rounded once to the nearest float64; gamma = float32(sum / (N*K)) with a
+ * float64 division.  eps = 1e-5f; W / (gamma + eps) is an IEEE float32
+ * division; Round is round-half-to-even.  Deterministic: the result does not
+ * depend on launch shape or scheduling.
+ */
+int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K,
+                               uint32_t* packed, float* gamma,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- a3: per-token AbsMax INT8 activation quantisation ------------------ */
+/*
+ * gamma_A[m] = max_k |X[m,k]|                                   [PMV s1, AbsMax]
+ * Xq[m,k]    = Clip(Round(X[m,k] * (127 / (gamma_A[m] + eps))), -128, 127)
+ * rowsum[m]  = sum_k Xq[m,k] (exact)
+ *
+ * X:       device [M, K] float32 or bfloat16 (x_dtype), aligned to its element
+ *          size (rows of any length; 16-byte alignment of X together with
+ *          K*sizeof % 16 == 0 selects 16-byte loads).
+ * Xq:      device int8 [M, Kp] (output); columns K..Kp-1 are written as 0.
+ *          16-byte aligned.
+ * gamma_a: device float32 [M] (output).  rowsum: device int32 [M] (output).
+ *
+ * Arithmetic: float32; s = 127 / (gamma_A + 1e-5f) is one IEEE division per
+ * token, each code is rint(X * s) (half to even) clipped to [-128, 127].
+ */
+int bitlinear_quantize_activations(const void* X, int x_dtype, int64_t M, int64_t K,
+                                   int8_t* Xq, float* gamma_a, int32_t* rowsum,
+                                   void* stream);
+
+/* ---- a3..a6: the forward ------------------------------------------------ */
+/*
+ * Y[m,n] = (sum_k Xq[m,k] * q[n,k]) * gamma * gamma_A[m] / 127
+ *          [PMV s2: add for +1, subtract for -1, skip for 0; INT32 accumulator;
+ *           one rescale by gamma_A * gamma / 127]
+ *
+ * X:      device [M, K] float32 or bfloat16, aligned to its element size.
+ * packed: device packed codes of an [N, K] ternary matrix, 16-byte aligned.
+ * gamma:  device float32[1], the weight scale from bitlinear_quantize_weights.
+ * Y:      device float32 [M, N] (output), 4-byte aligned.
+ * workspace: device, >= bitlinear_forward_workspace_bytes(M, K) when the
+ *         prefill path runs (M > bitlinear_max_decode_m() or
+ *         M*(Kp+16) > bitlinear_max_decode_codes()),
+ *         256-byte aligned; may be NULL/0 on the decode path.
+ *
+ * The INT32 accumulator is exact (|acc| <= 127 * K); Y is acc converted to
+ * float32 times the float32 product gamma * gamma_A[m] / 127 (three float32
+ * roundings in all, relative error < 2e-7).
+ */
+int bitlinear_forward(const void* X, int x_dtype, int64_t M, int64_t K,
+                      const uint32_t* packed, int64_t N, const float* gamma,
+                      float* Y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Same as bitlinear_forward with two additions for tests and benchmarks:
+ *   path:  BITLINEAR_PATH_AUTO / _DECODE / _PREFILL (forcing decode with M or
+ *          M*(Kp+16) beyond its limits returns BITLINEAR_ERR_SHAPE);
+ *   acc:   if not NULL, device int32 [M, N] receiving the exact accumulator
+ *          sum_k Xq[m,k] * q[n,k] as well (Y is still written).
+ */
+int bitlinear_forward_ex(const void* X, int x_dtype, int64_t M, int64_t K,
+                         const uint32_t* packed, int64_t N, const float* gamma,
+                         float* Y, int32_t* acc, int path,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * L independent decode forwards of one shape in one launch (the decode path's
+ * batched form: e.g. several projections of one token batch, or the experts
+ * of a layer).  Layer l reads X + l*M*K elements, packed + l*N*Kp/16 words,
+ * gamma[l], and writes Y + l*M*N; all 16-byte aligned as above.
+ * Requires M <= bitlinear_max_decode_m() and
+ * M*(Kp+16) <= bitlinear_max_decode_codes().
+ */
+int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, int64_t K,
+                              const uint32_t* packed, int64_t N, const float* gamma,
+                              float* Y, void* stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* bitlinear_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

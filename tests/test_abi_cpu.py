@@ -1,0 +1,140 @@
+"""The C ABI on the host: the library loads, exports every function the header
+declares, sizes are right, and every argument check fires before any HIP call
+(no kernel is launched here: this runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bitlinear_absmean_ternarise_bit_amd import abi
+from bitlinear_absmean_ternarise_bit_amd.build import LIB_PATH, build_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+P = ctypes.c_void_p
+FAKE = P(4096)  # a non-null, 256-byte aligned address: never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        build_library()
+    return abi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(abi.SIGNATURES)
+
+
+def test_sizes(lib):
+    assert lib.bitlinear_padded_k(1) == 64
+    assert lib.bitlinear_padded_k(64) == 64
+    assert lib.bitlinear_padded_k(65) == 128
+    assert lib.bitlinear_padded_k(0) == 0
+    assert lib.bitlinear_packed_bytes(2048, 2048) == 2048 * 2048 // 4  # 0.25 byte per weight
+    assert lib.bitlinear_packed_bytes(3, 100) == 3 * 128 // 4
+    assert lib.bitlinear_packed_bytes(0, 5) == 0
+    assert 0 < lib.bitlinear_quantize_workspace_bytes() < 128 * 1024
+    assert lib.bitlinear_forward_workspace_bytes(10, 100) >= 10 * 128 + 80
+    assert lib.bitlinear_forward_workspace_bytes(10, 100) % 256 == 0
+    assert lib.bitlinear_max_decode_m() == 16
+    assert lib.bitlinear_max_decode_codes() == 65536
+
+
+def test_status_strings(lib):
+    for s in range(-7, 1):
+        assert abi.status_string(s)
+    assert abi.status_string(-99) == "unknown status"
+
+
+def test_quantize_weights_checks(lib):
+    ws = lib.bitlinear_quantize_workspace_bytes()
+    f = lib.bitlinear_quantize_weights
+    assert f(None, 4, 4, FAKE, FAKE, FAKE, ws, None) == abi.ERR_NULL
+    assert f(FAKE, 4, 4, None, FAKE, FAKE, ws, None) == abi.ERR_NULL
+    assert f(FAKE, 4, 4, FAKE, None, FAKE, ws, None) == abi.ERR_NULL
+    assert f(FAKE, 0, 4, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE
+    assert f(FAKE, 4, -1, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE
+    assert f(FAKE, 4, (1 << 20) + 1, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE
+    assert f(FAKE, 1 << 13, 1 << 19, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE  # N*K >= 2^32
+    assert f(P(4100), 4, 4, FAKE, FAKE, FAKE, ws, None) == abi.ERR_ALIGN
+    assert f(FAKE, 4, 4, P(4104), FAKE, FAKE, ws, None) == abi.ERR_ALIGN
+    assert f(FAKE, 4, 4, FAKE, P(4098), FAKE, ws, None) == abi.ERR_ALIGN
+    assert f(FAKE, 4, 4, FAKE, FAKE, None, ws, None) == abi.ERR_WORKSPACE
+    assert f(FAKE, 4, 4, FAKE, FAKE, FAKE, ws - 1, None) == abi.ERR_WORKSPACE
+    assert f(FAKE, 4, 4, FAKE, FAKE, P(4100), ws, None) == abi.ERR_ALIGN
+
+
+def test_quantize_activations_checks(lib):
+    f = lib.bitlinear_quantize_activations
+    assert f(None, 0, 2, 8, FAKE, FAKE, FAKE, None) == abi.ERR_NULL
+    assert f(FAKE, 0, 2, 8, FAKE, None, FAKE, None) == abi.ERR_NULL
+    assert f(FAKE, 2, 2, 8, FAKE, FAKE, FAKE, None) == abi.ERR_DTYPE
+    assert f(FAKE, -1, 2, 8, FAKE, FAKE, FAKE, None) == abi.ERR_DTYPE
+    assert f(FAKE, 0, 0, 8, FAKE, FAKE, FAKE, None) == abi.ERR_SHAPE
+    assert f(FAKE, 0, 2, 0, FAKE, FAKE, FAKE, None) == abi.ERR_SHAPE
+    assert f(P(4098), 0, 2, 8, FAKE, FAKE, FAKE, None) == abi.ERR_ALIGN  # f32 needs 4 bytes
+    assert f(P(4097), 1, 2, 8, FAKE, FAKE, FAKE, None) == abi.ERR_ALIGN  # bf16 needs 2 bytes
+    assert f(FAKE, 0, 2, 8, P(4100), FAKE, FAKE, None) == abi.ERR_ALIGN
+
+
+def test_forward_checks(lib):
+    f = lib.bitlinear_forward_ex
+    wsb = lib.bitlinear_forward_workspace_bytes(64, 128)
+    args = dict(X=FAKE, dt=0, M=64, K=128, packed=FAKE, N=32, gamma=FAKE, Y=FAKE, acc=None,
+                path=0, ws=FAKE, wsb=wsb)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["X"], a["dt"], a["M"], a["K"], a["packed"], a["N"], a["gamma"], a["Y"], a["acc"],
+                 a["path"], a["ws"], a["wsb"], None)
+
+    assert call(X=None) == abi.ERR_NULL
+    assert call(packed=None) == abi.ERR_NULL
+    assert call(gamma=None) == abi.ERR_NULL
+    assert call(Y=None) == abi.ERR_NULL
+    assert call(M=0) == abi.ERR_SHAPE
+    assert call(N=0) == abi.ERR_SHAPE
+    assert call(K=0) == abi.ERR_SHAPE
+    assert call(dt=7) == abi.ERR_DTYPE
+    assert call(path=3) == abi.ERR_ARG
+    assert call(packed=P(4104)) == abi.ERR_ALIGN
+    assert call(Y=P(4098)) == abi.ERR_ALIGN
+    assert call(acc=P(4098)) == abi.ERR_ALIGN
+    # prefill path (M > 16) needs the workspace
+    assert call(ws=None) == abi.ERR_WORKSPACE
+    assert call(wsb=wsb - 1) == abi.ERR_WORKSPACE
+    assert call(ws=P(4096 + 16)) == abi.ERR_ALIGN
+    # forcing decode beyond its limits
+    assert call(path=1) == abi.ERR_SHAPE  # M = 64 > 16
+    assert call(M=16, K=4096, path=1) == abi.ERR_SHAPE  # 16 * (4096 + 16) > 65536
+    g = lib.bitlinear_forward
+    assert g(FAKE, 0, 64, 128, FAKE, 32, FAKE, FAKE, None, 0, None) == abi.ERR_WORKSPACE
+
+
+def test_forward_batched_checks(lib):
+    f = lib.bitlinear_forward_batched
+    assert f(0, FAKE, 1, 1, 2048, FAKE, 2048, FAKE, FAKE, None) == abi.ERR_SHAPE
+    assert f(4, None, 1, 1, 2048, FAKE, 2048, FAKE, FAKE, None) == abi.ERR_NULL
+    assert f(4, FAKE, 1, 17, 2048, FAKE, 2048, FAKE, FAKE, None) == abi.ERR_SHAPE
+    assert f(4, FAKE, 5, 1, 2048, FAKE, 2048, FAKE, FAKE, None) == abi.ERR_DTYPE
+    assert f(4, FAKE, 1, 1, 2048, P(4100), 2048, FAKE, FAKE, None) == abi.ERR_ALIGN
+
+
+def test_header_documents_citations_and_conventions():
+    text = open(HEADER).read()
+    for fn in declared_functions():
+        assert fn in text
+    assert "PMV" in text and "DEVICE pointers" in text
