@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Benchmark of the BitNet b1.58 BitLinear forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Default workload: decode, M=1 token, K=2048, N=2048 (a d_model-2048
+projection), bfloat16 activations, packed ternary weights.  One launch of the
+decode kernel is far below HBM latency for a single 1 MiB matrix, so a step is
+the batched decode forward over a pool of L distinct layers of that shape
+(each with its own weights, activations and outputs; >= 1 GiB of packed
+weights, several times the 256 MB last-level cache, so every byte comes from
+HBM).  The metric is GB/s of algorithmic bytes (packed weights + activations +
+outputs) against the 8 TB/s HBM3E peak.
+
+--workload prefill_ffn_m2048_k4096_n11008 (or the 8192x8192x28672 one) times
+the prefill forward instead (activation quantiser + INT8-MFMA GEMM) and
+reports INT8 TOPS (2*M*N*K per step) against the 5.0 POPS dense INT8 peak.
+
+Weight quantisation (absmean + ternarise + pack) runs once per weight matrix
+before the timed region; it is timed separately and reported under
+"weight_quantisation".
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+--copy-calibration runs a plain 1 GiB device copy (for HBM counter scaling).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA, TOPS
+METRIC = "BitLinear fwd: decode GEMV GB/s (% HBM peak); prefill INT8 TOPS (% MFMA peak)"
+
+DECODE_WORKLOADS = {"decode_m1_k2048_n2048": 0.02, "decode_ffn_up_m8_k2048_n5632": 0.02}
+PREFILL_WORKLOADS = ("prefill_ffn_m2048_k4096_n11008", "prefill_ffn_m8192_k8192_n28672")
+
+# HBM bytes per launch of the dominant kernel, read from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE counter runs and scaled by the same counters on a plain 1 GiB copy.
+# Valid only while the kernel sources hash to `sources_sha` (else traffic = null).
+TRAFFIC = {}
+
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "quant_act.hpp", "common.hpp"],
+    "prefill": ["prefill.hip", "common.hpp"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sources_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "bitlinear_absmean_ternarise_bit_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str, kind: str):
+    t = TRAFFIC.get(workload)
+    if not t or t["sources_sha"] != sources_sha(kind):
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+class Timer:
+    """HIP events on the current stream (the stream every binding call launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.torch.cuda.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def bench_decode(args, torch, bl, dev):
+    import numpy as np
+    from bitlinear_absmean_ternarise_bit_amd.workloads import make_workload
+
+    sigma = DECODE_WORKLOADS[args.workload]
+    P = make_workload(args.workload)
+    M, K, N = P.M, P.K, P.N
+    words = bl.packed_words(K)
+    packed_bytes = N * words * 4
+    L = args.layers or max(8, -(-(1 << 30) // packed_bytes))  # >= 1 GiB of packed weights
+    log(f"[bench] decode {args.workload}: M={M} K={K} N={N}, pool of {L} layers "
+        f"({L * packed_bytes / 2**30:.2f} GiB packed)")
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    # weights: layer 0 is the seeded numpy draw of the workload, the rest torch's seeded device RNG
+    W = torch.empty((L, N, K), dtype=torch.float32, device=dev)
+    W[0].copy_(torch.from_numpy(P.W))
+    W[1:].normal_(0.0, sigma, generator=g)
+    X = torch.empty((L, M, K), dtype=torch.bfloat16, device=dev)
+    X[0].copy_(torch.from_numpy(P.X_bf16_bits.view(np.int16)).view(torch.bfloat16))
+    X[1:].copy_(torch.randn((L - 1, M, K), generator=g, device=dev).to(torch.bfloat16))
+    if P.name == "decode_ffn_up_m8_k2048_n5632":  # same 1% outlier channels x20 in every layer
+        ch = torch.from_numpy(P.notes["outlier_channels"]).to(dev)
+        X[1:, :, ch] = (X[1:, :, ch].float() * 20.0).to(torch.bfloat16)
+    packed = torch.empty((L, N, words), dtype=torch.int32, device=dev)
+    gamma = torch.empty((L,), dtype=torch.float32, device=dev)
+    ws = torch.empty((bl.abi.load().bitlinear_quantize_workspace_bytes(),), dtype=torch.uint8, device=dev)
+    Y = torch.empty((L, M, N), dtype=torch.float32, device=dev)
+
+    # offline: weight quantisation of the whole pool (timed, not part of the step)
+    with Timer(torch) as tq:
+        for l in range(L):
+            bl.quantize_weights(W[l], out_packed=packed[l], out_gamma=gamma[l:l + 1], workspace=ws)
+    wq_bytes = L * (4 * N * K + N * words * 4)
+    log(f"[bench] weight quantisation of {L} layers: {tq.ms:.1f} ms")
+    del W
+    torch.cuda.empty_cache()
+
+    for _ in range(args.warmup):
+        bl.forward_batched(X, packed, gamma, K, out=Y)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    with Timer(torch) as t:
+        for _ in range(args.steps):
+            bl.forward_batched(X, packed, gamma, K, out=Y)
+    ms_step = t.ms / args.steps
+    step_bytes = L * (N * words * 4 + M * K * 2 + M * N * 4)
+    gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {gbps:.1f} GB/s")
+
+    # one layer per call, rotating over the pool (cold weights): the latency-bound single call
+    Y1 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    R = min(L, 256)
+    for l in range(8):
+        bl.forward(X[l], packed[l], gamma[l:l + 1], K, out=Y1)
+    with Timer(torch) as t1:
+        for l in range(R):
+            bl.forward(X[l], packed[l], gamma[l:l + 1], K, out=Y1)
+    single_us = t1.ms / R * 1e3
+    layer_bytes = step_bytes // L
+
+    out = {
+        "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s",
+        "ms_per_step": round(ms_step, 6),
+        "dtype": "i8",
+        "config": {"workload": f"{args.workload} x {L} layers per step (batched decode, cold weights)",
+                   "M": M, "K": K, "N": N, "layers": L, "x_dtype": "bf16",
+                   "bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_for(args.workload, "decode"),
+                     "kernel": "decode_kernel (fused quantise + GEMV + rescale), one launch per step"},
+        "single_call": {"us": round(single_us, 2), "GBps": round(layer_bytes / (single_us * 1e-6) / 1e9, 2),
+                        "note": "one layer per launch, cold weights"},
+        "weight_quantisation": {"ms_per_matrix": round(tq.ms / L, 4),
+                                "GBps": round(wq_bytes / (tq.ms * 1e-3) / 1e9, 2),
+                                "bytes_per_matrix": wq_bytes // L,
+                                "note": "absmean + ternarise + pack, offline, not in the step"},
+    }
+    if args.cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(P, layer_bytes, args.cpu_seconds)
+    return out
+
+
+def cpu_baseline_decode(P, layer_bytes, seconds):
+    import oracle as O
+    gamma, q, _ = O.quantize_weights(P.W)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.forward_from_codes(P.X, q, gamma)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    log(f"[bench] cpu oracle: {reps} forwards of layer 0 in {el:.1f} s")
+    return {"value": round(reps * layer_bytes / el / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"layer 0 of the pool ({P.name}, seed 0): the oracle's forward from ternary "
+                      f"codes (absmax quantise + exact contraction + rescale) repeated {reps} times"}
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def bench_prefill(args, torch, bl, dev):
+    import numpy as np
+    from bitlinear_absmean_ternarise_bit_amd.workloads import make_workload
+
+    P = make_workload(args.workload)
+    M, K, N = P.M, P.K, P.N
+    log(f"[bench] prefill {args.workload}: M={M} K={K} N={N}")
+    W = torch.from_numpy(P.W).to(dev)
+    with Timer(torch) as tq:
+        packed, gamma = bl.quantize_weights(W)
+    del W
+    torch.cuda.empty_cache()
+    X = torch.from_numpy(P.X_bf16_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws_bytes = bl.abi.load().bitlinear_forward_workspace_bytes(M, K)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        bl.forward(X, packed, gamma, K, out=Y, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    with Timer(torch) as t:
+        for _ in range(args.steps):
+            bl.forward(X, packed, gamma, K, out=Y, workspace=ws)
+    ms_step = t.ms / args.steps
+    ops = 2.0 * M * N * K
+    tops = ops / (ms_step * 1e-3) / 1e12
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {tops:.1f} TOPS")
+
+    # dominant kernel alone: the GEMM + rescale from precomputed codes
+    Xq, ga, rs = bl.quantize_activations(X)
+    for _ in range(2):
+        bl.forward_quantized(Xq, ga, rs, packed, gamma, K, out=Y)
+    with Timer(torch) as tg:
+        for _ in range(args.steps):
+            bl.forward_quantized(Xq, ga, rs, packed, gamma, K, out=Y)
+    gemm_ms = tg.ms / args.steps
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    step_bytes = N * bl.packed_words(K) * 4 + M * K * 2 + M * N * 4
+    out = {
+        "metric": METRIC, "value": round(tops, 2), "unit": "TOPS",
+        "ms_per_step": round(ms_step, 6),
+        "dtype": "i8",
+        "config": {"workload": args.workload, "M": M, "K": K, "N": N, "x_dtype": "bf16",
+                   "ops_per_step": ops, "bytes_per_step": step_bytes},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
+                     "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": traffic_for(args.workload, "prefill"),
+                     "kernel": "prefill_gemm_kernel (INT8 MFMA + fused rescale)",
+                     "kernel_ms": round(gemm_ms, 6)},
+        "weight_quantisation": {"ms_per_matrix": round(tq.ms, 4),
+                                "GBps": round((4 * N * K + N * bl.packed_words(K) * 4) / (tq.ms * 1e-3) / 1e9, 2),
+                                "note": "absmean + ternarise + pack, offline, not in the step"},
+    }
+    if args.cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_prefill(P, args.cpu_seconds)
+    return out
+
+
+def cpu_baseline_prefill(P, seconds):
+    import numpy as np
+    import oracle as O
+    gamma, q, _ = O.quantize_weights(P.W)
+    rows_per_rep = 32
+    cols = np.arange(P.N)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        r0 = (reps * rows_per_rep) % P.M
+        O.sampled_forward(P.X, q, gamma, np.arange(r0, r0 + rows_per_rep), cols)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    ops = 2.0 * reps * rows_per_rep * P.N * P.K
+    log(f"[bench] cpu oracle: {reps} x {rows_per_rep} tokens in {el:.1f} s")
+    return {"value": round(ops / el / 1e12, 6), "unit": "TOPS", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{reps * rows_per_rep} of {P.M} tokens x all {P.N} outputs of {P.name}: "
+                      f"the oracle's forward from ternary codes, {rows_per_rep} tokens per call"}
+
+
+# ---------------------------------------------------------------------------
+
+def copy_calibration(torch, dev):
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    log("[bench] copy calibration: 3 x elementwise add of 1 GiB (1 GiB read + 1 GiB written each)")
+    print(json.dumps({"copy_calibration_bytes_read": 1 << 30, "copy_calibration_bytes_written": 1 << 30}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_m1_k2048_n2048",
+                    choices=sorted(DECODE_WORKLOADS) + list(PREFILL_WORKLOADS))
+    ap.add_argument("--layers", type=int, default=0, help="decode pool size (default: >= 1 GiB packed)")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the BitLinear forward shards over tokens or output channels without changes to "
+              "the kernel); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bitlinear_absmean_ternarise_bit_amd as bl
+
+    dev = torch.device("cuda:0")
+    bl.abi.load()
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return
+    if args.workload in DECODE_WORKLOADS:
+        out = bench_decode(args, torch, bl, dev)
+    else:
+        out = bench_prefill(args, torch, bl, dev)
+    line = {"metric": out.pop("metric"), "value": out.pop("value"), "unit": out.pop("unit"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": out.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": out.pop("dtype"), "data": "synthetic (seeded)",
+            "config": out.pop("config")}
+    line.update(out)
+    line["device"] = torch.cuda.get_device_name(dev)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,6 +22,7 @@ __all__ = [
     "quantize_activations",
     "forward",
     "forward_batched",
+    "forward_quantized",
     "max_decode_m",
     "decode_fits",
 ]
@@ -81,10 +82,11 @@ def _x_dtype(X):
     raise ValueError("X must be float32 or bfloat16")
 
 
-def quantize_weights(W):
+def quantize_weights(W, out_packed=None, out_gamma=None, workspace=None):
     """AbsMean ternarisation + 2-bit packing of a float32 [N, K] GPU tensor.
 
-    Returns (packed int32 [N, padded_k(K) // 16] holding uint32 words, gamma float32 [1]).
+    Returns (packed int32 [N, padded_k(K) // 16] holding uint32 words, gamma float32 [1]);
+    ``out_packed`` / ``out_gamma`` / ``workspace`` may be given to avoid allocations.
     """
     torch = _torch()
     _require_cuda(W, "W")
@@ -92,10 +94,20 @@ def quantize_weights(W):
         raise ValueError("W must be a float32 [N, K] tensor")
     lib = abi.load()
     N, K = W.shape
-    packed = torch.empty((N, packed_words(K)), dtype=torch.int32, device=W.device)
-    gamma = torch.empty((1,), dtype=torch.float32, device=W.device)
-    ws_bytes = lib.bitlinear_quantize_workspace_bytes()
-    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
+    packed = out_packed if out_packed is not None else torch.empty(
+        (N, packed_words(K)), dtype=torch.int32, device=W.device)
+    gamma = out_gamma if out_gamma is not None else torch.empty((1,), dtype=torch.float32,
+                                                                device=W.device)
+    if packed.shape != (N, packed_words(K)) or packed.element_size() != 4 or gamma.numel() < 1:
+        raise ValueError("output buffers have the wrong shape")
+    _require_cuda(packed, "out_packed")
+    if workspace is not None:
+        _require_cuda(workspace, "workspace")
+        ws = workspace
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        ws_bytes = lib.bitlinear_quantize_workspace_bytes()
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
     abi.check("bitlinear_quantize_weights",
               lib.bitlinear_quantize_weights(_ptr(W), N, K, _ptr(packed), _ptr(gamma), _ptr(ws),
                                              ws_bytes, _stream(W)))
@@ -156,6 +168,28 @@ def forward(X, packed, gamma, K: int | None = None, path: str = "auto", return_a
               lib.bitlinear_forward_ex(_ptr(X), _x_dtype(X), M, K, _ptr(packed), N, _ptr(gamma),
                                        _ptr(Y), _ptr(acc), _PATHS[path], _ptr(ws), ws_bytes,
                                        _stream(X)))
+    return (Y, acc) if return_acc else Y
+
+
+def forward_quantized(Xq, gamma_a, rowsum, packed, gamma, K: int, return_acc: bool = False, out=None):
+    """Contraction + rescale from activation codes (as quantize_activations returns them)."""
+    torch = _torch()
+    for t, nm in ((Xq, "Xq"), (gamma_a, "gamma_a"), (rowsum, "rowsum"), (packed, "packed"),
+                  (gamma, "gamma")):
+        _require_cuda(t, nm)
+    M = Xq.shape[0]
+    if Xq.dtype != torch.int8 or Xq.shape[1] != padded_k(K):
+        raise ValueError("Xq must be int8 [M, padded_k(K)]")
+    N = packed.shape[0]
+    if packed.shape[1] != packed_words(K):
+        raise ValueError("packed does not hold padded_k(K) // 16 words per row")
+    lib = abi.load()
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device) if return_acc else None
+    abi.check("bitlinear_forward_quantized",
+              lib.bitlinear_forward_quantized(_ptr(Xq), _ptr(gamma_a), _ptr(rowsum), M, K,
+                                              _ptr(packed), N, _ptr(gamma), _ptr(Y), _ptr(acc),
+                                              _stream(Xq)))
     return (Y, acc) if return_acc else Y
 
 

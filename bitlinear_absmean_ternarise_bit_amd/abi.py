@@ -42,6 +42,7 @@ SIGNATURES = {
     "bitlinear_quantize_activations": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p]),
     "bitlinear_forward": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _sz, _p]),
     "bitlinear_forward_ex": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _int, _p, _sz, _p]),
+    "bitlinear_forward_quantized": (_int, [_p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p]),
     "bitlinear_forward_batched": (_int, [_i64, _p, _int, _i64, _i64, _p, _i64, _p, _p, _p]),
     "bitlinear_status_string": (ctypes.c_char_p, [_int]),
 }

@@ -137,6 +137,19 @@ int bitlinear_forward(const void* X, int x_dtype, int64_t M, int64_t K, const ui
                               workspace, workspace_bytes, stream);
 }
 
+int bitlinear_forward_quantized(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum,
+                                int64_t M, int64_t K, const uint32_t* packed, int64_t N,
+                                const float* gamma, float* Y, int32_t* acc, void* stream) {
+  if (!Xq || !gamma_a || !rowsum || !packed || !gamma || !Y) return BITLINEAR_ERR_NULL;
+  int st = check_mnk(M, N, K);
+  if (st) return st;
+  if (!aligned(Xq, 16) || !aligned(gamma_a, 4) || !aligned(rowsum, 4) || !aligned(packed, 16) ||
+      !aligned(gamma, 4) || !aligned(Y, 4) || (acc && !aligned(acc, 4)))
+    return BITLINEAR_ERR_ALIGN;
+  return hip_status(launch_prefill_gemm(Xq, gamma_a, rowsum, M, K, packed, N, gamma, Y, acc,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, int64_t K,
                               const uint32_t* packed, int64_t N, const float* gamma, float* Y,
                               void* stream) {

@@ -163,6 +163,22 @@ int bitlinear_forward_ex(const void* X, int x_dtype, int64_t M, int64_t K,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The contraction and rescale alone, from activation codes that are already
+ * quantised (by bitlinear_quantize_activations, or by a producer kernel that
+ * writes the same format):  Y = (Xq x q^T) * gamma * gamma_A / 127   [PMV s2]
+ *
+ * Xq:      device int8 [M, Kp], 16-byte aligned; columns K..Kp-1 must be 0.
+ * gamma_a: device float32 [M].  rowsum: device int32 [M], the exact sum of
+ *          each token's codes (the kernel forms sum c*x with c = q + 1 and
+ *          subtracts it).
+ * packed, gamma, Y, acc: as for bitlinear_forward_ex.  Runs the INT8-MFMA
+ * GEMM for any M.
+ */
+int bitlinear_forward_quantized(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum,
+                                int64_t M, int64_t K, const uint32_t* packed, int64_t N,
+                                const float* gamma, float* Y, int32_t* acc, void* stream);
+
+/*
  * L independent decode forwards of one shape in one launch (the decode path's
  * batched form: e.g. several projections of one token batch, or the experts
  * of a layer).  Layer l reads X + l*M*K elements, packed + l*N*Kp/16 words,

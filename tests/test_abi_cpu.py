@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(abi.SIGNATURES)
@@ -122,6 +122,15 @@ def test_forward_checks(lib):
     assert call(M=16, K=4096, path=1) == abi.ERR_SHAPE  # 16 * (4096 + 16) > 65536
     g = lib.bitlinear_forward
     assert g(FAKE, 0, 64, 128, FAKE, 32, FAKE, FAKE, None, 0, None) == abi.ERR_WORKSPACE
+
+
+def test_forward_quantized_checks(lib):
+    f = lib.bitlinear_forward_quantized
+    assert f(None, FAKE, FAKE, 4, 64, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_NULL
+    assert f(FAKE, FAKE, None, 4, 64, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 0, 64, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_SHAPE
+    assert f(P(4104), FAKE, FAKE, 4, 64, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, 4, 64, FAKE, 8, FAKE, FAKE, P(4098), None) == abi.ERR_ALIGN
 
 
 def test_forward_batched_checks(lib):

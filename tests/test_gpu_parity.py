@@ -197,6 +197,19 @@ def test_decode_and_prefill_agree_bitwise():
     assert torch.equal(Yd, Yp)
 
 
+def test_forward_quantized_matches_forward():
+    P = random_problem(70, 333, 140, seed=31, x_dtype="bf16")
+    W = torch.from_numpy(P.W).to(DEV)
+    X = dev_x(P)
+    packed, gamma = bl.quantize_weights(W)
+    Xq, ga, rs = bl.quantize_activations(X)
+    Yq, aq = bl.forward_quantized(Xq, ga, rs, packed, gamma, P.K, return_acc=True)
+    Yf, af = bl.forward(X, packed, gamma, P.K, path="prefill", return_acc=True)
+    torch.cuda.synchronize()
+    assert torch.equal(aq, af) and torch.equal(Yq, Yf)
+    assert np.array_equal(aq.cpu().numpy(), O.bitlinear_forward(P.X, P.W)["acc"])
+
+
 def test_forward_deterministic():
     P = random_problem(300, 700, 300, seed=4, x_dtype="bf16")
     W = torch.from_numpy(P.W).to(DEV)
