@@ -65,6 +65,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} is missing: build the HIP library first "
             "(python -m bitlinear_absmean_ternarise_bit_amd.build)")
+    # Load torch's HIP runtime first when torch is present: the library then
+    # binds to that same runtime, so streams and device pointers from torch are
+    # valid in its launches (a second runtime in the process would not share them).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -11,6 +11,7 @@ constexpr float kEps = 1e-5f;  // eps of both quantisers, a float32 constant
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -9,138 +9,236 @@
 // the exact token code sum is subtracted in the epilogue
 // (sum_k q x = sum_k c x - sum_k x).
 //
-// Tiling: a 256-thread workgroup owns a 256 (tokens) x 256 (weight rows)
-// output tile; its four waves each own 128 x 128 (4 x 4 MFMA tiles of
-// 32 x 32).  K advances 128 per step through two LDS stages: activation codes
-// [256][128] (rows padded to 144 bytes) and packed words [256][8] (rows
-// padded to 48 bytes), so 8 consecutive lanes reading 16 bytes each touch
-// distinct banks.
+// Tiling: a 256-thread workgroup owns a BM (tokens) x BN (weight rows) output
+// tile; its four waves form a 2 x 2 grid of (BM/2) x (BN/2) sub-tiles made of
+// 32 x 32 MFMA tiles.  K advances 128 per stage through two LDS stages.
+// Global loads run two stages ahead into two register sets (buffer loads with
+// 32-bit offsets; rows past M or N read as zeros from the hardware bounds
+// check), and the stage after the one being contracted is written to LDS
+// halfway through the contraction, so one barrier per stage suffices and the
+// matrix cores keep working while loads and LDS writes are in flight.
+//
+// LDS layout per stage: activation codes [BM][128 B] and packed words
+// [BN][32 B], both dense.  Bank conflicts are removed by XOR swizzles of the
+// 16-byte slots (activation slot c of row r lives at c ^ (r & 7); packed slot
+// c of row r at c ^ ((r >> 2) & 1)).
 //
 // MFMA operands: for 32x32x32 int8, lane l supplies 16 bytes of A row l % 32
-// and of B column l % 32, for the same 16 k positions (chosen by l / 32).  In
-// K step s (32 k) of a 128-k stage, lane group h = l / 32 uses packed word
-// 4h + s of its weight row (16 weights) and the 16 activation codes at
-// k = 64h + 16s of its token row: the same k on both sides.
+// and of B column l % 32 for the same 16 k positions (chosen by h = l / 32).
+// In K step s (0..3) of a stage, lane half h uses packed word
+// w(s, h) = 4 (s / 2) + 2 h + s % 2 of its weight row (16 weights) and the
+// 16 activation codes at k = 16 w(s, h) of its token row: the same k on both
+// sides.  Steps 0 and 1 use words 0..3 only, so a final half stage (Kp not a
+// multiple of 128) just skips steps 2 and 3.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace bitlinear {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int A_STRIDE = BK + 16;       // bytes per activation row in LDS
-constexpr int B_STRIDE = 48;            // bytes per packed weight row in LDS (32 used)
-constexpr int A_BYTES = BM * A_STRIDE;  // 36864
-constexpr int B_BYTES = BN * B_STRIDE;  // 12288
-constexpr int STAGE = A_BYTES + B_BYTES;
+constexpr int BK = 128;
+#ifndef PF_WM
+#define PF_WM 4
+#define PF_WN 2
+#endif
 
-template <bool WRITE_ACC>
-__global__ __launch_bounds__(256, 1) void prefill_gemm_kernel(
+// Buffer resource word 3 for raw (unformatted, stride 0) accesses on gfx9.
+constexpr int kBufferFlags = 0x00020000;
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most n LDS operations
+// are outstanding (vector-memory and export counters left free).
+constexpr int lgkmcnt_imm(int n) { return 15 | (3 << 14) | (7 << 4) | ((n & 15) << 8); }
+
+template <int BM, int BN, int WM, int WN, bool WRITE_ACC>
+__global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ gamma_a,
     const int32_t* __restrict__ rowsum, int64_t M, int64_t Kp, const uint32_t* __restrict__ packed,
     int64_t N, const float* __restrict__ gamma, float* __restrict__ Y, int32_t* __restrict__ acc,
-    int tiles_n) {
-  __shared__ __align__(16) char smem[2 * STAGE];
+    int tiles_m, int tiles_n, int bytes_a, int bytes_b) {
+  constexpr int A_BYTES = BM * 128;
+  constexpr int B_BYTES = BN * 32;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int THREADS = 64 * WM * WN;
+  constexpr int MI = BM / WM / 32;      // 32-row MFMA tiles per wave
+  constexpr int NI = BN / WN / 32;      // 32-column MFMA tiles per wave
+  constexpr int A_LOADS = BM * 8 / THREADS;  // 16-byte loads per thread per stage (activations)
+  constexpr int B_LOADS = BN * 2 / THREADS;  // (packed words)
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && MI >= 1 && NI >= 1, "tile too small for the workgroup");
+  __shared__ __align__(1024) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tm = blockIdx.x / tiles_n;
-  const int tn = blockIdx.x - tm * tiles_n;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // Workgroup -> tile.  Workgroups are dealt round-robin to the 8 XCDs; give
+  // each XCD a contiguous run of tiles, walked in groups of 8 tile rows so the
+  // tiles resident on one XCD share activation and weight panels in its L2.
+  const int num_tiles = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if (num_tiles % 8 == 0) t = (t & 7) * (num_tiles >> 3) + (t >> 3);
+  constexpr int GROUP = 8;
+  const int group = t / (GROUP * tiles_n);
+  const int first_m = group * GROUP;
+  const int gsize = min(tiles_m - first_m, GROUP);
+  const int in_group = t - group * GROUP * tiles_n;
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
   const int64_t m0 = static_cast<int64_t>(tm) * BM;
   const int64_t n0 = static_cast<int64_t>(tn) * BN;
-  const int64_t words = Kp >> 4;
-  const int niter = static_cast<int>((Kp + BK - 1) / BK);
 
-  // global -> register staging: A 8 x 16 B per thread, B 2 x 16 B per thread
-  uint4 ra[8], rb[2];
-  const int a_row = tid >> 3, a_col = tid & 7;  // + 32 p rows
-  const int b_row = tid >> 1, b_half = tid & 1; // + 128 p rows
+  // Global sources: buffer resources over the whole code arrays, 32-bit lane
+  // offsets; rows past M or N fall outside the resource and read as zeros
+  // (their outputs are discarded).  In a final half stage the slots past Kp
+  // re-read the 64 weights before them; they only reach the skipped steps.
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(Xq), 0, bytes_a, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsrc_b =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(packed), 0, bytes_b, kBufferFlags);
+  const uint32_t kp32 = static_cast<uint32_t>(Kp);
+  // thread -> 16-byte slots: activation slot tid + THREADS q is row
+  // (tid >> 3) + (THREADS / 8) q, logical column tid & 7; packed slot
+  // tid + THREADS q is row (tid >> 1) + (THREADS / 2) q, half tid & 1
+  const int a_r = tid >> 3, a_c = tid & 7;
+  const int b_r = tid >> 1, b_c = tid & 1;
+  const uint32_t voff_a = static_cast<uint32_t>(m0 + a_r) * kp32 + 16u * a_c;
+  const uint32_t voff_b = static_cast<uint32_t>(n0 + b_r) * (kp32 >> 2) + 16u * b_c;
+  const uint32_t a_row_step = (THREADS / 8) * kp32;          // rows of activation codes per q
+  const uint32_t b_row_step = (THREADS / 2) * (kp32 >> 2);   // rows of packed words per q
+  // LDS destinations (swizzled)
+  int a_dst[A_LOADS], b_dst[B_LOADS];
+#pragma unroll
+  for (int q = 0; q < A_LOADS; ++q) {
+    const int r = a_r + (THREADS / 8) * q;
+    a_dst[q] = r * 128 + 16 * (a_c ^ (r & 7));
+  }
+#pragma unroll
+  for (int q = 0; q < B_LOADS; ++q) {
+    const int r = b_r + (THREADS / 2) * q;
+    b_dst[q] = A_BYTES + r * 32 + 16 * (b_c ^ ((r >> 2) & 1));
+  }
 
-  auto gload = [&](int it) {
-    const int64_t k0 = static_cast<int64_t>(it) * BK;
+  v4u ra[2][A_LOADS], rb[2][B_LOADS];
+  auto gload = [&](int it, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
+    const uint32_t k0 = static_cast<uint32_t>(it) * BK;
+    const uint32_t a_adj = (k0 + 16u * a_c >= kp32) ? 64u : 0u;
+    const uint32_t b_adj = (k0 + 64u * b_c >= kp32) ? 16u : 0u;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int64_t m = m0 + a_row + 32 * p;
-      const int64_t kk = k0 + 16 * a_col;
-      ra[p] = (m < M && kk < Kp) ? *reinterpret_cast<const uint4*>(Xq + m * Kp + kk)
-                                 : make_uint4(0, 0, 0, 0);
-    }
+    for (int q = 0; q < A_LOADS; ++q)
+      ra[S][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a + k0 - a_adj, q * a_row_step, 0);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int64_t n = n0 + b_row + 128 * p;
-      const int64_t w = (k0 >> 4) + 4 * b_half;
-      rb[p] = (n < N && w < words) ? *reinterpret_cast<const uint4*>(packed + n * words + w)
-                                   : make_uint4(0, 0, 0, 0);
-    }
+    for (int q = 0; q < B_LOADS; ++q)
+      rb[S][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b + (k0 >> 2) - b_adj, q * b_row_step, 0);
   };
-  auto sstore = [&](int buf) {
-    char* sa = smem + buf * STAGE;
-    char* sb = sa + A_BYTES;
+  auto swrite = [&](char* st, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
-      *reinterpret_cast<uint4*>(sa + (a_row + 32 * p) * A_STRIDE + 16 * a_col) = ra[p];
+    for (int q = 0; q < A_LOADS; ++q) *reinterpret_cast<v4u*>(st + a_dst[q]) = ra[S][q];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      *reinterpret_cast<uint4*>(sb + (b_row + 128 * p) * B_STRIDE + 16 * b_half) = rb[p];
+    for (int q = 0; q < B_LOADS; ++q) *reinterpret_cast<v4u*>(st + b_dst[q]) = rb[S][q];
   };
 
-  v16i c[4][4];
+  v16i c[MI][NI];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) c[mi][ni][r] = 0;
 
   const int lr = lane & 31;
   const int lh = lane >> 5;
+  // LDS byte offsets of this lane's operands within a stage.  The swizzle
+  // terms depend on lr only (tile row bases are multiples of 8), so tile mi /
+  // ni adds a constant that the ds_read instruction carries as its offset.
+  int a_off[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int cl = 4 * (s >> 1) + 2 * lh + (s & 1);
+    a_off[s] = (wm * (BM / WM) + lr) * 128 + 16 * (cl ^ (lr & 7));
+  }
+  int b_off[2];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs)
+    b_off[hs] = A_BYTES + (wn * (BN / WN) + lr) * 32 + 16 * (hs ^ ((lr >> 2) & 1)) + 8 * lh;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int it = 0; it < niter; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < niter) gload(it + 1);
-    const char* sa = smem + buf * STAGE;
-    const char* sb = sa + A_BYTES;
-    uint4 bw[4];
+  // Contract half hs (steps 2hs, 2hs+1: 64 k) of an LDS stage.
+  auto contract_half = [&](const char* st, int hs) {
+    uint2 bw[NI];
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      bw[ni] = *reinterpret_cast<const uint4*>(sb + (wn * 128 + ni * 32 + lr) * B_STRIDE + 16 * lh);
+    for (int ni = 0; ni < NI; ++ni) bw[ni] = *reinterpret_cast<const uint2*>(st + b_off[hs] + ni * 1024);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      v4i a[4];
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int s = 2 * hs + s2;
+      v4i a[MI];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        a[mi] = *reinterpret_cast<const v4i*>(sa + (wm * 128 + mi * 32 + lr) * A_STRIDE + 64 * lh + 16 * s);
+      for (int mi = 0; mi < MI; ++mi) a[mi] = *reinterpret_cast<const v4i*>(st + a_off[s] + mi * 4096);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const uint32_t wd = s == 0 ? bw[ni].x : s == 1 ? bw[ni].y : s == 2 ? bw[ni].z : bw[ni].w;
-        const v4i b = unpack_word(wd);
+      for (int ni = 0; ni < NI; ++ni) {
+        const v4i b = unpack_word(s2 == 0 ? bw[ni].x : bw[ni].y);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
           c[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[mi], b, c[mi][ni], 0, 0, 0);
       }
     }
-    if (it + 1 < niter) sstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  const int nfull = static_cast<int>(Kp / BK);
+  const int niter = static_cast<int>((Kp + BK - 1) / BK);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  // prologue: stage 0 -> LDS 0; stage 1 in register set 1; stage 2 loading into set 0
+  gload(0, S0());
+  gload(min(1, niter - 1), S1());
+  swrite(smem, S0());
+  gload(min(2, niter - 1), S0());
+  __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // Iteration it contracts LDS stage it % 2; halfway it writes stage it + 1
+  // (register set (it + 1) % 2, loaded two iterations earlier) into the other
+  // LDS stage and reloads that register set with stage it + 3.  Past the last
+  // stage the write lands in the idle LDS stage and the reload repeats the last
+  // stage: harmless, and the loop stays free of branches, which keeps the
+  // compiler's count of outstanding loads exact (it then waits only for the
+  // older register set).
+  auto iteration = [&](int it, auto set_tag) {
+    const char* cur = smem + (it & 1) * STAGE;
+    char* nxt = smem + ((it + 1) & 1) * STAGE;
+    contract_half(cur, 0);
+    swrite(nxt, set_tag);
+    gload(min(it + 3, niter - 1), set_tag);
+    contract_half(cur, 1);
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // LDS traffic stays on its side of the barrier
+  };
+  int it = 0;
+  for (; it + 1 < nfull; it += 2) {
+    iteration(it, S1());
+    iteration(it + 1, S0());
   }
+  if (it < nfull) iteration(it, S1());
+  if (nfull < niter) contract_half(smem + (nfull & 1) * STAGE, 0);  // final half stage
 
   // epilogue: lane holds rows 8*(r/4) + 4*(l/32) + r%4, column l%32 of each 32x32 tile
   const float gm = gamma[0];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+  for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t m = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      const int64_t m = m0 + wm * (BM / WM) + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
       if (m >= M) continue;
       const int rs = rowsum[m];
       const float scale = __fdiv_rn(__fmul_rn(gm, gamma_a[m]), 127.0f);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int64_t n = n0 + wn * 128 + ni * 32 + lr;
+      for (int ni = 0; ni < NI; ++ni) {
+        const int64_t n = n0 + wn * (BN / WN) + ni * 32 + lr;
         if (n < N) {
           const int v = c[mi][ni][r] - rs;
           if constexpr (WRITE_ACC) acc[m * N + n] = v;
@@ -151,22 +249,51 @@ __global__ __launch_bounds__(256, 1) void prefill_gemm_kernel(
   }
 }
 
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_tile(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum, int64_t M,
+                       int64_t Kp, const uint32_t* packed, int64_t N, const float* gamma, float* Y,
+                       int32_t* acc, hipStream_t stream) {
+  // Buffer offsets are 32-bit: run the tokens in chunks of < 2^31 code bytes.
+  const int64_t chunk = ((int64_t(1) << 31) - 1) / Kp / BM * BM;
+  const int bytes_b = static_cast<int>(N * (Kp / 4));
+  for (int64_t r0 = 0; r0 < M; r0 += chunk) {
+    const int64_t Mc = min(M - r0, chunk);
+    const int tiles_m = static_cast<int>((Mc + BM - 1) / BM);
+    const int tiles_n = static_cast<int>((N + BN - 1) / BN);
+    const unsigned blocks = static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n);
+    const int bytes_a = static_cast<int>(Mc * Kp);
+    if (acc)
+      prefill_gemm_kernel<BM, BN, WM, WN, true><<<blocks, 64 * WM * WN, 0, stream>>>(
+          Xq + r0 * Kp, gamma_a + r0, rowsum + r0, Mc, Kp, packed, N, gamma, Y + r0 * N, acc + r0 * N,
+          tiles_m, tiles_n, bytes_a, bytes_b);
+    else
+      prefill_gemm_kernel<BM, BN, WM, WN, false><<<blocks, 64 * WM * WN, 0, stream>>>(
+          Xq + r0 * Kp, gamma_a + r0, rowsum + r0, Mc, Kp, packed, N, gamma, Y + r0 * N, nullptr,
+          tiles_m, tiles_n, bytes_a, bytes_b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_prefill_gemm(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum,
                                int64_t M, int64_t K, const uint32_t* packed, int64_t N,
                                const float* gamma, float* Y, int32_t* acc, hipStream_t stream) {
   const int64_t Kp = padded_k(K);
-  const int tiles_m = static_cast<int>((M + BM - 1) / BM);
-  const int tiles_n = static_cast<int>((N + BN - 1) / BN);
-  const unsigned blocks = static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n);
-  if (acc)
-    prefill_gemm_kernel<true><<<blocks, 256, 0, stream>>>(Xq, gamma_a, rowsum, M, Kp, packed, N,
-                                                          gamma, Y, acc, tiles_n);
-  else
-    prefill_gemm_kernel<false><<<blocks, 256, 0, stream>>>(Xq, gamma_a, rowsum, M, Kp, packed, N,
-                                                           gamma, Y, acc, tiles_n);
-  return hipGetLastError();
+  // One workgroup per CU; pick the tile whose rounds over 256 CUs cost least
+  // (work per tile is proportional to its area), larger tile on ties.
+  auto cost = [&](int64_t bm, int64_t bn) {
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    return ((tiles + 255) / 256) * bm * bn;
+  };
+  const int64_t c256 = cost(256, 256), c128 = cost(256, 128), c64 = cost(128, 128);
+  if (c256 <= c128 && c256 <= c64)
+    return launch_tile<256, 256, PF_WM, PF_WN>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
+  if (c128 <= c64)
+    return launch_tile<256, 128, 2, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
+  return launch_tile<128, 128, 2, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
 }
 
 }  // namespace bitlinear
