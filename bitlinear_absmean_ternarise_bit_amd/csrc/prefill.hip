@@ -9,19 +9,21 @@
 // the exact token code sum is subtracted in the epilogue
 // (sum_k q x = sum_k c x - sum_k x).
 //
-// Tiling: a 256-thread workgroup owns a BM (tokens) x BN (weight rows) output
-// tile; its four waves form a 2 x 2 grid of (BM/2) x (BN/2) sub-tiles made of
-// 32 x 32 MFMA tiles.  K advances 128 per stage through two LDS stages.
+// Tiling: a workgroup of WM x WN waves owns a BM (tokens) x BN (weight rows)
+// output tile; each wave owns a (BM/WM) x (BN/WN) sub-tile made of 32 x 32
+// MFMA tiles (256 x 256 with 4 x 2 waves for large problems).  K advances 128 per stage through two LDS stages.
 // Global loads run two stages ahead into two register sets (buffer loads with
 // 32-bit offsets; rows past M or N read as zeros from the hardware bounds
 // check), and the stage after the one being contracted is written to LDS
 // halfway through the contraction, so one barrier per stage suffices and the
 // matrix cores keep working while loads and LDS writes are in flight.
 //
-// LDS layout per stage: activation codes [BM][128 B] and packed words
-// [BN][32 B], both dense.  Bank conflicts are removed by XOR swizzles of the
-// 16-byte slots (activation slot c of row r lives at c ^ (r & 7); packed slot
-// c of row r at c ^ ((r >> 2) & 1)).
+// LDS layout per stage: activation codes [BM][128 B], dense, with 16-byte
+// slot c of row r stored at slot c ^ ((r >> 1) & 7), so the 16 lanes that one
+// LDS cycle serves (16 consecutive rows, same logical slot) hit 16 distinct
+// bank groups; packed words as [hs][h][BN] 8-byte pairs (words 4hs + 2h and
+// 4hs + 2h + 1 of every row contiguous), so the 32 lanes of a 64-bit read
+// cover 256 contiguous bytes.
 //
 // MFMA operands: for 32x32x32 int8, lane l supplies 16 bytes of A row l % 32
 // and of B column l % 32 for the same 16 k positions (chosen by h = l / 32).
@@ -39,10 +41,6 @@ namespace bitlinear {
 namespace {
 
 constexpr int BK = 128;
-#ifndef PF_WM
-#define PF_WM 4
-#define PF_WN 2
-#endif
 
 // Buffer resource word 3 for raw (unformatted, stride 0) accesses on gfx9.
 constexpr int kBufferFlags = 0x00020000;
@@ -64,8 +62,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
   constexpr int MI = BM / WM / 32;      // 32-row MFMA tiles per wave
   constexpr int NI = BN / WN / 32;      // 32-column MFMA tiles per wave
   constexpr int A_LOADS = BM * 8 / THREADS;  // 16-byte loads per thread per stage (activations)
-  constexpr int B_LOADS = BN * 2 / THREADS;  // (packed words)
-  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && MI >= 1 && NI >= 1, "tile too small for the workgroup");
+  constexpr int B_SLOTS = BN * 2;            // 16-byte packed slots per stage
+  constexpr int B_LOADS = B_SLOTS >= THREADS ? B_SLOTS / THREADS : 1;
+  constexpr bool B_ALL = B_SLOTS >= THREADS;  // else only threads < B_SLOTS load packed words
+  static_assert(A_LOADS >= 1 && MI >= 1 && NI >= 1, "tile too small for the workgroup");
   __shared__ __align__(1024) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -108,16 +108,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
   const uint32_t a_row_step = (THREADS / 8) * kp32;          // rows of activation codes per q
   const uint32_t b_row_step = (THREADS / 2) * (kp32 >> 2);   // rows of packed words per q
   // LDS destinations (swizzled)
-  int a_dst[A_LOADS], b_dst[B_LOADS];
+  int a_dst[A_LOADS], b_dst[B_LOADS];  // b_dst: LDS offset of the slot's first 8-byte half
 #pragma unroll
   for (int q = 0; q < A_LOADS; ++q) {
     const int r = a_r + (THREADS / 8) * q;
-    a_dst[q] = r * 128 + 16 * (a_c ^ (r & 7));
+    a_dst[q] = r * 128 + 16 * (a_c ^ ((r >> 1) & 7));
   }
 #pragma unroll
   for (int q = 0; q < B_LOADS; ++q) {
     const int r = b_r + (THREADS / 2) * q;
-    b_dst[q] = A_BYTES + r * 32 + 16 * (b_c ^ ((r >> 2) & 1));
+    b_dst[q] = A_BYTES + ((2 * b_c) * BN + r) * 8;  // words 4c, 4c+1; words 4c+2, 4c+3 at +BN*8
   }
 
   v4u ra[2][A_LOADS], rb[2][B_LOADS];
@@ -131,14 +131,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
       ra[S][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a + k0 - a_adj, q * a_row_step, 0);
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q)
-      rb[S][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b + (k0 >> 2) - b_adj, q * b_row_step, 0);
+      if (B_ALL || tid < B_SLOTS)
+        rb[S][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b + (k0 >> 2) - b_adj, q * b_row_step, 0);
   };
   auto swrite = [&](char* st, auto set_tag) {
     constexpr int S = decltype(set_tag)::value;
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q) *reinterpret_cast<v4u*>(st + a_dst[q]) = ra[S][q];
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) *reinterpret_cast<v4u*>(st + b_dst[q]) = rb[S][q];
+    for (int q = 0; q < B_LOADS; ++q)
+      if (B_ALL || tid < B_SLOTS) {
+        *reinterpret_cast<uint2*>(st + b_dst[q]) = make_uint2(rb[S][q][0], rb[S][q][1]);
+        *reinterpret_cast<uint2*>(st + b_dst[q] + BN * 8) = make_uint2(rb[S][q][2], rb[S][q][3]);
+      }
   };
 
   v16i c[MI][NI];
@@ -158,31 +163,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int cl = 4 * (s >> 1) + 2 * lh + (s & 1);
-    a_off[s] = (wm * (BM / WM) + lr) * 128 + 16 * (cl ^ (lr & 7));
+    a_off[s] = (wm * (BM / WM) + lr) * 128 + 16 * (cl ^ ((lr >> 1) & 7));
   }
   int b_off[2];
 #pragma unroll
-  for (int hs = 0; hs < 2; ++hs)
-    b_off[hs] = A_BYTES + (wn * (BN / WN) + lr) * 32 + 16 * (hs ^ ((lr >> 2) & 1)) + 8 * lh;
+  for (int hs = 0; hs < 2; ++hs) b_off[hs] = A_BYTES + ((2 * hs + lh) * BN + wn * (BN / WN) + lr) * 8;
 
-  // Contract half hs (steps 2hs, 2hs+1: 64 k) of an LDS stage.
+  // Contract half hs (steps 2hs, 2hs+1: 64 k) of an LDS stage.  The packed
+  // words of both steps are read first, and the activation operands of the
+  // second step are requested before the first step's MFMAs are issued, so
+  // LDS latency overlaps matrix-core work.
   auto contract_half = [&](const char* st, int hs) {
     uint2 bw[NI];
+    v4i a0[MI], a1[MI];
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) bw[ni] = *reinterpret_cast<const uint2*>(st + b_off[hs] + ni * 1024);
+    for (int ni = 0; ni < NI; ++ni) bw[ni] = *reinterpret_cast<const uint2*>(st + b_off[hs] + ni * 256);
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int s = 2 * hs + s2;
-      v4i a[MI];
+    for (int mi = 0; mi < MI; ++mi) a0[mi] = *reinterpret_cast<const v4i*>(st + a_off[2 * hs] + mi * 4096);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) a[mi] = *reinterpret_cast<const v4i*>(st + a_off[s] + mi * 4096);
+    for (int mi = 0; mi < MI; ++mi) a1[mi] = *reinterpret_cast<const v4i*>(st + a_off[2 * hs + 1] + mi * 4096);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const v4i b = unpack_word(s2 == 0 ? bw[ni].x : bw[ni].y);
+    for (int ni = 0; ni < NI; ++ni) {
+      const v4i b = unpack_word(bw[ni].x);
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          c[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[mi], b, c[mi][ni], 0, 0, 0);
-      }
+      for (int mi = 0; mi < MI; ++mi)
+        c[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[mi], b, c[mi][ni], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const v4i b = unpack_word(bw[ni].y);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        c[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[mi], b, c[mi][ni], 0, 0, 0);
     }
   };
 
@@ -282,17 +294,14 @@ hipError_t launch_prefill_gemm(const int8_t* Xq, const float* gamma_a, const int
                                int64_t M, int64_t K, const uint32_t* packed, int64_t N,
                                const float* gamma, float* Y, int32_t* acc, hipStream_t stream) {
   const int64_t Kp = padded_k(K);
-  // One workgroup per CU; pick the tile whose rounds over 256 CUs cost least
-  // (work per tile is proportional to its area), larger tile on ties.
-  auto cost = [&](int64_t bm, int64_t bn) {
-    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-    return ((tiles + 255) / 256) * bm * bn;
-  };
-  const int64_t c256 = cost(256, 256), c128 = cost(256, 128), c64 = cost(128, 128);
-  if (c256 <= c128 && c256 <= c64)
-    return launch_tile<256, 256, PF_WM, PF_WN>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
-  if (c128 <= c64)
-    return launch_tile<256, 128, 2, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
+  // One workgroup per CU.  The 256 x 256 tile (8 waves of 64 x 128) has the
+  // best ratio of matrix-core work to LDS traffic; smaller tiles are used only
+  // when the big one would leave more than a quarter of the 256 CUs idle.
+  auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (tiles(256, 256) >= 192)
+    return launch_tile<256, 256, 4, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
+  if (tiles(128, 256) >= 192)
+    return launch_tile<128, 256, 2, 4>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
   return launch_tile<128, 128, 2, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
 }
 

@@ -158,6 +158,8 @@ FORWARD_CASES = [
     (257, 200, 513, "f32", "prefill"),
     (512, 1088, 768, "bf16", "prefill"),
     (40, 4096, 1000, "bf16", "auto"),
+    (1024, 640, 6144, "bf16", "prefill"),   # 128 x 256 tiles
+    (2000, 1050, 6200, "f32", "prefill"),   # 256 x 256 tiles, ragged M, N and a half K stage
 ]
 
 
