@@ -46,7 +46,12 @@ PREFILL_WORKLOADS = ("prefill_ffn_m2048_k4096_n11008", "prefill_ffn_m8192_k8192_
 # HBM bytes per launch of the dominant kernel, read from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE counter runs and scaled by the same counters on a plain 1 GiB copy.
 # Valid only while the kernel sources hash to `sources_sha` (else traffic = null).
-TRAFFIC = {}
+TRAFFIC = {
+    # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on `bench.py --steps 3 --warmup 1`
+    # (1024-layer batched decode launch); scale factors 2.0 / 1.0 from the
+    # 1 GiB copy of `bench.py --copy-calibration` (524,300 KiB read, 1,048,576 KiB written)
+    "decode_m1_k2048_n2048": {"sources_sha": "724f4d3efe57edc4", "fetch_bytes": 1084473440, "write_bytes": 10402608},
+}
 
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "quant_act.hpp", "common.hpp"],
