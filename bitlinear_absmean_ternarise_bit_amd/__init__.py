@@ -68,9 +68,12 @@ def max_decode_m() -> int:
     return int(abi.load().bitlinear_max_decode_m())
 
 
-def decode_fits(M: int, K: int) -> bool:
+def decode_fits(M: int, K: int, N: int) -> bool:
+    """Whether the decode kernel takes an M x K activation against N weight rows."""
     lib = abi.load()
-    return M <= lib.bitlinear_max_decode_m() and M * (padded_k(K) + 16) <= lib.bitlinear_max_decode_codes()
+    return (M <= lib.bitlinear_max_decode_m()
+            and M * (padded_k(K) + 16) <= lib.bitlinear_max_decode_codes()
+            and M * N < (1 << 29))
 
 
 def _x_dtype(X):
@@ -159,7 +162,7 @@ def forward(X, packed, gamma, K: int | None = None, path: str = "auto", return_a
     acc = torch.empty((M, N), dtype=torch.int32, device=X.device) if return_acc else None
     ws_bytes = 0
     ws = workspace
-    if ws is None and not (path == "decode" or (path == "auto" and decode_fits(M, K))):
+    if ws is None and not (path == "decode" or (path == "auto" and decode_fits(M, K, N))):
         ws_bytes = lib.bitlinear_forward_workspace_bytes(M, K)
         ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=X.device)
     elif ws is not None:

@@ -29,8 +29,10 @@ int check_x(const void* X, int x_dtype) {
   return BITLINEAR_OK;
 }
 
-bool decode_fits(int64_t M, int64_t K) {
-  return M <= kDecodeMaxM && M * (padded_k(K) + 16) <= kDecodeMaxCodes;
+// The decode kernel keeps all token codes in LDS and addresses a layer's
+// outputs with 32-bit offsets.
+bool decode_fits(int64_t M, int64_t K, int64_t N) {
+  return M <= kDecodeMaxM && M * (padded_k(K) + 16) <= kDecodeMaxCodes && M * N < (int64_t(1) << 29);
 }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -117,7 +119,7 @@ int bitlinear_forward_ex(const void* X, int x_dtype, int64_t M, int64_t K, const
     return BITLINEAR_ERR_ARG;
   if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(Y, 4) || (acc && !aligned(acc, 4)))
     return BITLINEAR_ERR_ALIGN;
-  const bool fits = decode_fits(M, K);
+  const bool fits = decode_fits(M, K, N);
   if (path == BITLINEAR_PATH_DECODE && !fits) return BITLINEAR_ERR_SHAPE;
   const bool decode = path == BITLINEAR_PATH_DECODE || (path == BITLINEAR_PATH_AUTO && fits);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -159,7 +161,7 @@ int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, 
   if (st) return st;
   st = check_x(X, x_dtype);
   if (st) return st;
-  if (!decode_fits(M, K)) return BITLINEAR_ERR_SHAPE;
+  if (!decode_fits(M, K, N)) return BITLINEAR_ERR_SHAPE;
   const int64_t bpl = (N + 63) / 64;
   if (L * bpl >= (int64_t(1) << 31)) return BITLINEAR_ERR_SHAPE;
   if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(Y, 4)) return BITLINEAR_ERR_ALIGN;

@@ -65,20 +65,39 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const int bpg = (chunks + kUnroll - 1) / kUnroll;                   // batches per row group
   const int nbatch = groups * bpg;
 
-  auto load_batch = [&](int b, uint4 (&r)[kUnroll]) {
+  // Packed rows are read, and outputs written, through buffer resources over
+  // this layer's arrays.  Every load and store is unconditional: offsets that
+  // must not touch memory (rows past N, words past a row's end, batches past
+  // the last, outputs that are not due yet) are set past the resource and the
+  // hardware bounds check turns them into zeros / dropped stores.  Without
+  // branches the compiler keeps the next batch of loads in flight while the
+  // current one is contracted.
+  constexpr uint32_t kOff = 0xfffffff0u;  // past every resource
+  const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(packed), 0, static_cast<int>(N * words * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ysrc = __builtin_amdgcn_make_buffer_rsrc(
+      Y, 0, static_cast<int>(static_cast<int64_t>(M) * N * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t asrc = __builtin_amdgcn_make_buffer_rsrc(
+      WRITE_ACC ? static_cast<void*>(acc) : static_cast<void*>(Y), 0,
+      WRITE_ACC ? static_cast<int>(static_cast<int64_t>(M) * N * 4) : 0, 0x00020000);
+  const uint32_t words32 = static_cast<uint32_t>(words);
+  const uint32_t N32 = static_cast<uint32_t>(N);
+  auto load_batch = [&](int b, bool valid, uint4 (&r)[kUnroll]) {
     const int gi = b / bpg;
     const int cb = b - gi * bpg;
-    const int64_t n = n_base + gi * kRowsPerWave + j;
-    const uint32_t* prow = packed + (n < N ? n : 0) * words;
+    const uint32_t row_off = static_cast<uint32_t>(n_base + gi * kRowsPerWave + j) * words32 * 4u;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t w0 = static_cast<int64_t>(cb * kUnroll + u) * 16 + 4 * g;
-      r[u] = (n < N && w0 < words) ? *reinterpret_cast<const uint4*>(prow + w0) : make_uint4(0, 0, 0, 0);
+      const uint32_t w0 = static_cast<uint32_t>(cb * kUnroll + u) * 16u + 4u * g;
+      const uint32_t off = (valid && w0 < words32) ? row_off + 4u * w0 : kOff;
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off, 0, 0);
+      r[u] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
 
   uint4 buf0[kUnroll], buf1[kUnroll];
-  load_batch(0, buf0);
+  load_batch(0, true, buf0);
+  __builtin_amdgcn_sched_barrier(0);
 
   // phase A: AbsMax INT8 codes of every token into LDS (one wave per token)
   for (int m = wave; m < M; m += kWaves) {
@@ -94,7 +113,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   __syncthreads();
 
   const bool avalid = j < M;
-  const int8_t* arow = sxq + j * lds_stride;
+  const int8_t* arow = sxq + (avalid ? j : 0) * lds_stride;
   const v4i zero = {0, 0, 0, 0};
   const float gm = gamma[0];
   v4i c = zero;
@@ -104,44 +123,47 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const int cb = b - gi * bpg;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t c0 = static_cast<int64_t>(cb * kUnroll + u) * 16;
-      if (c0 >= words) break;  // wave-uniform
-      const int64_t w0 = c0 + 4 * g;
-      const bool kvalid = w0 < words;
+      const uint32_t w0 = static_cast<uint32_t>(cb * kUnroll + u) * 16u + 4u * g;
+      const bool use = avalid && w0 < words32;
       const uint32_t wd[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const v4i bop = unpack_word(wd[t]);
-        const v4i a = (avalid && kvalid) ? *reinterpret_cast<const v4i*>(arow + 16 * (w0 + t)) : zero;
+        const v4i araw = *reinterpret_cast<const v4i*>(arow + (use ? 16u * (w0 + t) : 0u));
+        const v4i a = use ? araw : zero;
         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop, c, 0, 0, 0);
       }
     }
-    if (cb == bpg - 1) {
-      // epilogue: lane holds tokens 4g + r of weight row n
-      const int64_t n = n_base + gi * kRowsPerWave + j;
-      if (n < N) {
+    // epilogue of the row group after its last batch: lane holds tokens
+    // 4g + r of weight row n
+    const bool last = cb == bpg - 1;
+    const uint32_t n = static_cast<uint32_t>(n_base + gi * kRowsPerWave + j);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * g + r;
-          if (i < M) {
-            const int v = c[r] - s_rs[i];
-            if constexpr (WRITE_ACC) acc[static_cast<int64_t>(i) * N + n] = v;
-            const float scale = __fdiv_rn(__fmul_rn(gm, s_ga[i]), 127.0f);
-            Y[static_cast<int64_t>(i) * N + n] = __fmul_rn(static_cast<float>(v), scale);
-          }
-        }
-      }
-      c = zero;
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * g + r;
+      const int ic = i < M ? i : M - 1;
+      const int v = c[r] - s_rs[ic];
+      const float scale = __fdiv_rn(__fmul_rn(gm, s_ga[ic]), 127.0f);
+      const float y = __fmul_rn(static_cast<float>(v), scale);
+      const uint32_t off = (last && i < M && n < N32) ? (static_cast<uint32_t>(i) * N32 + n) * 4u : kOff;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), ysrc, off, 0, 0);
+      if constexpr (WRITE_ACC) __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(v), asrc, off, 0, 0);
     }
+    c = last ? zero : c;
   };
 
-  for (int b = 0; b < nbatch; b += 2) {
-    if (b + 1 < nbatch) load_batch(b + 1, buf1);
+  // sched_barrier keeps the scheduler from sinking a batch's loads into the
+  // contraction that follows them.
+  int b = 0;
+  for (; b + 1 < nbatch; b += 2) {
+    load_batch(b + 1, true, buf1);
+    __builtin_amdgcn_sched_barrier(0);
     contract(b, buf0);
-    if (b + 1 >= nbatch) break;
-    if (b + 2 < nbatch) load_batch(b + 2, buf0);
+    load_batch(b + 2, b + 2 < nbatch, buf0);
+    __builtin_amdgcn_sched_barrier(0);
     contract(b + 1, buf1);
   }
+  if (b < nbatch) contract(b, buf0);
 }
 
 // Rows per workgroup = 64 * groups.  Larger blocks quantise X less often and

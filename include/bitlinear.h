@@ -81,7 +81,7 @@ size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t K);
 
 /* Largest M the decode path accepts (16), and the largest M*(Kp+16) it
  * accepts (the codes of all tokens live in on-chip memory, each token row
- * padded by 16 bytes: 65536 bytes). */
+ * padded by 16 bytes: 65536 bytes).  The decode path also needs M*N < 2^29. */
 int bitlinear_max_decode_m(void);
 int64_t bitlinear_max_decode_codes(void);
 
