@@ -47,10 +47,14 @@ PREFILL_WORKLOADS = ("prefill_ffn_m2048_k4096_n11008", "prefill_ffn_m8192_k8192_
 # WRITE_SIZE counter runs and scaled by the same counters on a plain 1 GiB copy.
 # Valid only while the kernel sources hash to `sources_sha` (else traffic = null).
 TRAFFIC = {
-    # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on `bench.py --steps 3 --warmup 1`
-    # (1024-layer batched decode launch); scale factors 2.0 / 1.0 from the
-    # 1 GiB copy of `bench.py --copy-calibration` (524,300 KiB read, 1,048,576 KiB written)
-    "decode_m1_k2048_n2048": {"sources_sha": "724f4d3efe57edc4", "fetch_bytes": 1084473440, "write_bytes": 10402608},
+    # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of the dominant launch on
+    # `bench.py --workload W --steps 1 --warmup 1 --no-cpu-baseline`; scale factors
+    # 2.0 (FETCH_SIZE) and 1.0 (WRITE_SIZE) from the 1 GiB copy of
+    # `bench.py --copy-calibration` (524,306 KiB read, 1,048,576 KiB written).
+    "decode_m1_k2048_n2048": {"sources_sha": "6f1b2332de1ab21a", "fetch_bytes": 1087335778, "write_bytes": 10246976},
+    "decode_ffn_up_m8_k2048_n5632": {"sources_sha": "6f1b2332de1ab21a", "fetch_bytes": 1212439738, "write_bytes": 80068512},
+    "prefill_ffn_m2048_k4096_n11008": {"sources_sha": "c236d9a81221c5d2", "fetch_bytes": 149741097, "write_bytes": 90177536},
+    "prefill_ffn_m8192_k8192_n28672": {"sources_sha": "c236d9a81221c5d2", "fetch_bytes": 2200289666, "write_bytes": 939524096},
 }
 
 KERNEL_SOURCES = {

@@ -56,13 +56,26 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, 
   constexpr int P = ActTraits<DT>::kPerChunk;
   float mx = 0.0f;
   if constexpr (VEC) {
+    // four 16-byte loads in flight per lane; chunks past the row re-read the
+    // last chunk (in bounds) and are dropped by the select
     const uint4* r4 = static_cast<const uint4*>(row);
     const int64_t nc = K / P;
-    for (int64_t c = lane; c < nc; c += kWave) {
-      float f[P];
-      chunk_to_f32<DT>(r4[c], f);
+    for (int64_t c0 = lane; c0 < nc; c0 += 4 * kWave) {
+      uint4 v[4];
 #pragma unroll
-      for (int i = 0; i < P; ++i) mx = fmaxf(mx, fabsf(f[i]));
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + u * kWave;
+        v[u] = r4[c < nc ? c : nc - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float f[P];
+        chunk_to_f32<DT>(v[u], f);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < P; ++i) m = fmaxf(m, fabsf(f[i]));
+        mx = (c0 + u * kWave < nc) ? fmaxf(mx, m) : mx;
+      }
     }
   } else {
     for (int64_t k = lane; k < K; k += kWave) mx = fmaxf(mx, fabsf(load_one<DT>(row, k)));

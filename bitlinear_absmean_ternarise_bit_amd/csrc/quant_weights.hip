@@ -80,7 +80,17 @@ __global__ __launch_bounds__(256) void absmean_digits_kernel(const float* __rest
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) tmax = max(tmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmax), o, kWave)));
-  const uint32_t T0 = tmax ? tmax - 1u : 0u;
+  // (a wave whose first loads are all zero -- e.g. zeroed rows -- takes the
+  // window of magnitudes below 4, where trained and synthetic weights live)
+  uint32_t any = 0;
+  {
+    uint32_t t, lo, hi;
+    split_abs(first.x | first.y | first.z | first.w, t, lo, hi);
+    any = lo | hi;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) any |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(any), o, kWave));
+  const uint32_t T0 = any ? (tmax ? tmax - 1u : 0u) : 2u;
 
   DigitAcc acc;
   if (tid < n4) {
@@ -89,12 +99,24 @@ __global__ __launch_bounds__(256) void absmean_digits_kernel(const float* __rest
     add_abs(first.z, T0, acc, sdig);
     add_abs(first.w, T0, acc, sdig);
   }
-  for (uint64_t i = tid + stride; i < n4; i += stride) {
-    const uint4 v = W4[i];
-    add_abs(v.x, T0, acc, sdig);
-    add_abs(v.y, T0, acc, sdig);
-    add_abs(v.z, T0, acc, sdig);
-    add_abs(v.w, T0, acc, sdig);
+  // four independent 16-byte loads in flight per lane; indices past the end
+  // re-read the last vector and are then zeroed (no branches around loads)
+  const uint64_t last = n4 ? n4 - 1 : 0;
+  for (uint64_t i0 = tid + stride; i0 < n4; i0 += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t idx = i0 + u * stride;
+      const uint4 x = W4[idx < n4 ? idx : last];
+      v[u] = idx < n4 ? x : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      add_abs(v[u].x, T0, acc, sdig);
+      add_abs(v[u].y, T0, acc, sdig);
+      add_abs(v[u].z, T0, acc, sdig);
+      add_abs(v[u].w, T0, acc, sdig);
+    }
   }
   // scalar tail (n not a multiple of 4)
   const uint64_t tail = n4 << 2;
