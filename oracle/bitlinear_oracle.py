@@ -19,7 +19,9 @@ quantisation, the BitLinear layer and Zero-GEMM).  Its sections:
 * [PMV §2]  how BitLinear removes multiplications (Zero-GEMM): add for +1,
   subtract for -1, skip for 0, INT32 accumulation, the worked 8-element
   example, and the single rescale of A_q x W_q^T by gamma_A * gamma / 127;
-* [PMV §3]  the memory wall: 2-bit packing, 0.25 byte per weight.
+* [PMV §3]  the memory wall: 2-bit packing, 0.25 byte per weight;
+* [PMV §4]  how bitnet.cpp speeds up CPU inference: the 81-entry LUT figure
+  for four weights and the Radix-3 packing of five weights per byte.
 
 Readings where the article leaves a step open:
 
@@ -163,6 +165,96 @@ def unpack_codes(words: np.ndarray, K: int) -> np.ndarray:
     if np.any(out == 3):
         raise ValueError("unpack_codes: invalid 2-bit field (3)")
     return (out.reshape(N, nw * 16)[:, :K] - 1).astype(np.int8)
+
+
+# ---------------------------------------------------------------------------
+# Radix-3 packing: five ternary weights per byte  [PMV §4, Radix-3 packing]
+# ---------------------------------------------------------------------------
+#
+# The article fixes the count (five weights per byte, 3^5 = 243 <= 256, 1.60
+# bits per weight) and, through its LUT figure, that a group of ternary
+# weights is indexed as a base-3 number of the offset digits c = q + 1 (all -1
+# gives index 0, all 0 gives 40 and all +1 gives 80 for four weights).  The
+# rest is this library's reading:
+#
+# * v = sum_t c_t * 3^(4-t) over the byte's five weights, first weight most
+#   significant;
+# * the byte stores v scaled to the byte range, ceil(256 * v / 243): a
+#   one-to-one map of the 243 values (inverse v = floor(243 * byte / 256)),
+#   chosen so that a decoder can read the digits most-significant first by
+#   multiplying the byte, as a fraction of 256, by three;
+# * a row of K weights is padded with c = 1 (zero weights) to a multiple of 80;
+#   byte 4j + b of a row (b = 0..3) holds the weights k = 20j + 4t + b for
+#   t = 0..4, so 16-byte pieces of a row cover 80 consecutive weights.
+
+R3_UNIT = 80  # weights per 16 bytes of a radix-3 row
+R3_DIGITS = 5
+
+
+def r3_padded_k(K: int) -> int:
+    return ((K + R3_UNIT - 1) // R3_UNIT) * R3_UNIT
+
+
+def r3_packed_bytes(N: int, K: int) -> int:
+    return N * r3_padded_k(K) // R3_DIGITS
+
+
+def r3_value(c5) -> int:
+    """Base-3 number of five offset codes c in {0,1,2}, the first most significant."""
+    v = 0
+    for c in c5:
+        if c not in (0, 1, 2):
+            raise ValueError("r3_value: offset code outside {0, 1, 2}")
+        v = 3 * v + int(c)
+    return v
+
+
+def r3_byte(v: int) -> int:
+    """Stored byte of the base-3 value v in [0, 242]: ceil(256 v / 243)."""
+    if not 0 <= v <= 242:
+        raise ValueError("r3_byte: value outside [0, 242]")
+    return (256 * v + 242) // 243
+
+
+def r3_value_of_byte(b: int) -> int:
+    """Inverse of :func:`r3_byte`; raises for the 13 bytes that encode nothing."""
+    v = (243 * int(b)) >> 8
+    if r3_byte(v) != int(b):
+        raise ValueError("r3_value_of_byte: byte %d is not a radix-3 encoding" % b)
+    return v
+
+
+def pack_codes_r3(q: np.ndarray) -> np.ndarray:
+    """Pack ternary codes [N, K] into bytes [N, r3_padded_k(K) // 5] (layout above)."""
+    q = np.asarray(q)
+    N, K = q.shape
+    Kp = r3_padded_k(K)
+    c = np.ones((N, Kp), dtype=np.int64)
+    c[:, :K] = q.astype(np.int64) + 1
+    c = c.reshape(N, Kp // 20, R3_DIGITS, 4)  # [n, word j, digit t, byte b]: k = 20j + 4t + b
+    v = np.zeros((N, Kp // 20, 4), dtype=np.int64)
+    for t in range(R3_DIGITS):
+        v = 3 * v + c[:, :, t, :]
+    out = (256 * v + 242) // 243
+    return out.reshape(N, Kp // R3_DIGITS).astype(np.uint8)
+
+
+def unpack_codes_r3(packed: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of :func:`pack_codes_r3`; int8 codes [N, K] (raises on a byte that encodes nothing)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    N, nb = packed.shape
+    if nb % 4:
+        raise ValueError("unpack_codes_r3: row length is not a whole number of 4-byte words")
+    b = packed.astype(np.int64)
+    v = (243 * b) >> 8
+    if np.any((256 * v + 242) // 243 != b):
+        raise ValueError("unpack_codes_r3: byte that is not a radix-3 encoding")
+    v = v.reshape(N, nb // 4, 4)
+    c = np.empty((N, nb // 4, R3_DIGITS, 4), dtype=np.int64)
+    for t in range(R3_DIGITS - 1, -1, -1):  # least significant digit is the last weight
+        c[:, :, t, :] = v % 3
+        v = v // 3
+    return (c.reshape(N, nb * R3_DIGITS)[:, :K] - 1).astype(np.int8)
 
 
 # ---------------------------------------------------------------------------
