@@ -12,6 +12,9 @@ weights, several times the 256 MB last-level cache, so every byte comes from
 HBM).  The metric is GB/s of algorithmic bytes (packed weights + activations +
 outputs) against the 8 TB/s HBM3E peak.
 
+--format radix3 streams the weights packed five per byte (1.6 bits) through
+the same decode kernel; "weights_per_s" compares the two formats.
+
 --workload prefill_ffn_m2048_k4096_n11008 (or the 8192x8192x28672 one) times
 the prefill forward instead (activation quantiser + INT8-MFMA GEMM) and
 reports INT8 TOPS (2*M*N*K per step) against the 5.0 POPS dense INT8 peak.
@@ -116,19 +119,21 @@ class Timer:
 # decode
 # ---------------------------------------------------------------------------
 
-def bench_decode(args, torch, bl, dev):
+def build_decode_pool(torch, bl, dev, workload: str, L: int, fmt: str = "2bit", keep=()):
+    """The decode step's inputs: L layers of one workload shape, resident on the GPU.
+
+    Layer 0 is the workload's seeded numpy draw; the other layers come from
+    torch's seeded device generator (seed 1234) in the same distribution.  Weights
+    are quantised on the GPU (``fmt`` "2bit" or "radix3"), in chunks of layers;
+    the float32 weights of the layers in ``keep`` are returned on the host.
+    Returns (P, X, packed, gamma, tq_ms, kept) with tq_ms the quantisation time.
+    """
     import numpy as np
     from bitlinear_absmean_ternarise_bit_amd.workloads import make_workload
 
-    sigma = DECODE_WORKLOADS[args.workload]
-    P = make_workload(args.workload)
+    sigma = DECODE_WORKLOADS[workload]
+    P = make_workload(workload)
     M, K, N = P.M, P.K, P.N
-    words = bl.packed_words(K)
-    packed_bytes = N * words * 4
-    L = args.layers or max(8, -(-(1 << 30) // packed_bytes))  # >= 1 GiB of packed weights
-    log(f"[bench] decode {args.workload}: M={M} K={K} N={N}, pool of {L} layers "
-        f"({L * packed_bytes / 2**30:.2f} GiB packed)")
-
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
     X = torch.empty((L, M, K), dtype=torch.bfloat16, device=dev)
@@ -137,52 +142,87 @@ def bench_decode(args, torch, bl, dev):
     if P.name == "decode_ffn_up_m8_k2048_n5632":  # same 1% outlier channels x20 in every layer
         ch = torch.from_numpy(P.notes["outlier_channels"]).to(dev)
         X[1:, :, ch] = (X[1:, :, ch].float() * 20.0).to(torch.bfloat16)
-    packed = torch.empty((L, N, words), dtype=torch.int32, device=dev)
+    if fmt == "radix3":
+        packed = torch.empty((L, N, bl.r3_row_bytes(K)), dtype=torch.uint8, device=dev)
+        quant = bl.quantize_weights_r3
+    else:
+        packed = torch.empty((L, N, bl.packed_words(K)), dtype=torch.int32, device=dev)
+        quant = bl.quantize_weights
     gamma = torch.empty((L,), dtype=torch.float32, device=dev)
     ws = torch.empty((bl.abi.load().bitlinear_quantize_workspace_bytes(),), dtype=torch.uint8, device=dev)
-    Y = torch.empty((L, M, N), dtype=torch.float32, device=dev)
-
-    # weights: layer 0 is the seeded numpy draw of the workload, the rest torch's
-    # seeded device RNG, drawn and quantised in chunks of layers.  The
-    # quantisation (offline, not part of the step) is timed separately.
     chunk = max(1, min(L, (1 << 32) // (4 * N * K)))
     Wc = torch.empty((chunk, N, K), dtype=torch.float32, device=dev)
     tq_ms = 0.0
+    kept = {}
     for l0 in range(0, L, chunk):
         n = min(chunk, L - l0)
         Wc[:n].normal_(0.0, sigma, generator=g)
         if l0 == 0:
             Wc[0].copy_(torch.from_numpy(P.W))
+        for l in keep:
+            if l0 <= l < l0 + n:
+                kept[l] = Wc[l - l0].cpu().numpy()
         with Timer(torch) as tq:
             for l in range(n):
-                bl.quantize_weights(Wc[l], out_packed=packed[l0 + l], out_gamma=gamma[l0 + l:l0 + l + 1],
-                                    workspace=ws)
+                quant(Wc[l], out_packed=packed[l0 + l], out_gamma=gamma[l0 + l:l0 + l + 1], workspace=ws)
         tq_ms += tq.ms
-    wq_bytes = L * (4 * N * K + N * words * 4)
-    log(f"[bench] weight quantisation of {L} layers: {tq_ms:.1f} ms")
     del Wc
     torch.cuda.empty_cache()
+    return P, X, packed, gamma, tq_ms, kept
+
+
+def bench_decode(args, torch, bl, dev):
+    from bitlinear_absmean_ternarise_bit_amd.workloads import make_workload
+
+    r3 = args.format == "radix3"
+    P0 = make_workload(args.workload)
+    M, K, N = P0.M, P0.K, P0.N
+    row_bytes = bl.r3_row_bytes(K) if r3 else bl.packed_words(K) * 4
+    packed_bytes = N * row_bytes
+    L = args.layers or max(8, -(-(1 << 30) // packed_bytes))  # >= 1 GiB of packed weights
+    log(f"[bench] decode {args.workload} ({args.format}): M={M} K={K} N={N}, pool of {L} layers "
+        f"({L * packed_bytes / 2**30:.2f} GiB packed)")
+    # weights: quantisation is offline, not part of the step; timed separately
+    P, X, packed, gamma, tq_ms, _ = build_decode_pool(torch, bl, dev, args.workload, L, args.format)
+    Y = torch.empty((L, M, N), dtype=torch.float32, device=dev)
+    wq_bytes = L * (4 * N * K + packed_bytes)
+    log(f"[bench] weight quantisation of {L} layers: {tq_ms:.1f} ms")
+
+    if r3:
+        def step():
+            bl.forward_r3(X, packed, gamma, K, out=Y)
+
+        def single(l, out):
+            bl.forward_r3(X[l], packed[l], gamma[l:l + 1], K, out=out)
+    else:
+        def step():
+            bl.forward_batched(X, packed, gamma, K, out=Y)
+
+        def single(l, out):
+            bl.forward(X[l], packed[l], gamma[l:l + 1], K, out=out)
 
     for _ in range(args.warmup):
-        bl.forward_batched(X, packed, gamma, K, out=Y)
+        step()
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
     with Timer(torch) as t:
         for _ in range(args.steps):
-            bl.forward_batched(X, packed, gamma, K, out=Y)
+            step()
     ms_step = t.ms / args.steps
-    step_bytes = L * (N * words * 4 + M * K * 2 + M * N * 4)
+    step_bytes = L * (packed_bytes + M * K * 2 + M * N * 4)
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {gbps:.1f} GB/s")
+    gw_s = L * N * K / (ms_step * 1e-3) / 1e9
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {gbps:.1f} GB/s, "
+        f"{gw_s:.1f} G weights/s")
 
     # one layer per call, rotating over the pool (cold weights): the latency-bound single call
     Y1 = torch.empty((M, N), dtype=torch.float32, device=dev)
     R = min(L, 256)
     for l in range(8):
-        bl.forward(X[l], packed[l], gamma[l:l + 1], K, out=Y1)
+        single(l, Y1)
     with Timer(torch) as t1:
         for l in range(R):
-            bl.forward(X[l], packed[l], gamma[l:l + 1], K, out=Y1)
+            single(l, Y1)
     single_us = t1.ms / R * 1e3
     layer_bytes = step_bytes // L
 
@@ -192,11 +232,14 @@ def bench_decode(args, torch, bl, dev):
         "dtype": "i8",
         "config": {"workload": f"{args.workload} x {L} layers per step (batched decode, cold weights)",
                    "M": M, "K": K, "N": N, "layers": L, "x_dtype": "bf16",
+                   "weight_format": "radix-3, 5 weights per byte" if r3 else "2-bit",
                    "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_for(args.workload, "decode"),
+                     "traffic": traffic_for(args.workload + ("/radix3" if r3 else ""), "decode"),
                      "kernel": "decode_kernel (fused quantise + GEMV + rescale), one launch per step"},
+        "weights_per_s": {"value": round(gw_s, 2), "unit": "G weights/s",
+                          "note": "N*K*layers per step / step time: compares weight formats"},
         "single_call": {"us": round(single_us, 2), "GBps": round(layer_bytes / (single_us * 1e-6) / 1e9, 2),
                         "note": "one layer per launch, cold weights"},
         "weight_quantisation": {"ms_per_matrix": round(tq_ms / L, 4),
@@ -330,6 +373,8 @@ def main():
     ap.add_argument("--workload", default="decode_m1_k2048_n2048",
                     choices=sorted(DECODE_WORKLOADS) + list(PREFILL_WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="decode pool size (default: >= 1 GiB packed)")
+    ap.add_argument("--format", default="2bit", choices=["2bit", "radix3"],
+                    help="decode weight format: 2-bit codes or radix-3 (five weights per byte)")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -349,6 +394,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, dev)
         return
+    if args.format != "2bit" and args.workload not in DECODE_WORKLOADS:
+        print("--format radix3 applies to the decode workloads only", file=sys.stderr)
+        sys.exit(2)
     if args.workload in DECODE_WORKLOADS:
         out = bench_decode(args, torch, bl, dev)
     else:

@@ -25,6 +25,11 @@ __all__ = [
     "forward_quantized",
     "max_decode_m",
     "decode_fits",
+    "r3_padded_k",
+    "r3_row_bytes",
+    "r3_decode_fits",
+    "quantize_weights_r3",
+    "forward_r3",
 ]
 
 
@@ -216,3 +221,92 @@ def forward_batched(X, packed, gamma, K: int | None = None, out=None):
               lib.bitlinear_forward_batched(L, _ptr(X), _x_dtype(X), M, K, _ptr(packed), N,
                                             _ptr(gamma), _ptr(Y), _stream(X)))
     return Y
+
+
+# ---- radix-3 weights (five per byte) --------------------------------------
+
+def r3_padded_k(K: int) -> int:
+    return int(abi.load().bitlinear_r3_padded_k(K))
+
+
+def r3_row_bytes(K: int) -> int:
+    """Bytes per radix-3 packed row."""
+    return r3_padded_k(K) // 5
+
+
+def r3_decode_fits(M: int, K: int, N: int) -> bool:
+    lib = abi.load()
+    return (M <= lib.bitlinear_max_decode_m()
+            and M * (r3_padded_k(K) + 16) <= lib.bitlinear_max_decode_codes()
+            and M * N < (1 << 29))
+
+
+def quantize_weights_r3(W, out_packed=None, out_gamma=None, workspace=None):
+    """AbsMean ternarisation of a float32 [N, K] GPU tensor, packed five weights per byte.
+
+    Returns (packed uint8 [N, r3_row_bytes(K)], gamma float32 [1]); gamma and the
+    ternary codes are bit-identical to :func:`quantize_weights`.
+    """
+    torch = _torch()
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a float32 [N, K] tensor")
+    lib = abi.load()
+    N, K = W.shape
+    packed = out_packed if out_packed is not None else torch.empty(
+        (N, r3_row_bytes(K)), dtype=torch.uint8, device=W.device)
+    gamma = out_gamma if out_gamma is not None else torch.empty((1,), dtype=torch.float32,
+                                                                device=W.device)
+    if packed.shape != (N, r3_row_bytes(K)) or packed.element_size() != 1 or gamma.numel() < 1:
+        raise ValueError("output buffers have the wrong shape")
+    _require_cuda(packed, "out_packed")
+    if workspace is not None:
+        _require_cuda(workspace, "workspace")
+        ws = workspace
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        ws_bytes = lib.bitlinear_quantize_workspace_bytes()
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
+    abi.check("bitlinear_quantize_weights_r3",
+              lib.bitlinear_quantize_weights_r3(_ptr(W), N, K, _ptr(packed), _ptr(gamma), _ptr(ws),
+                                                ws_bytes, _stream(W)))
+    return packed, gamma
+
+
+def forward_r3(X, packed, gamma, K: int | None = None, return_acc: bool = False, out=None):
+    """Decode forward over radix-3 weights.
+
+    X [M, K] with packed [N, r3_row_bytes(K)] and gamma [1], or X [L, M, K] with
+    packed [L, N, r3_row_bytes(K)] and gamma [L] (L layers in one launch).
+    Returns Y float32 [M, N] / [L, M, N] (and the INT32 accumulators if asked).
+    """
+    torch = _torch()
+    for t, nm in ((X, "X"), (packed, "packed"), (gamma, "gamma")):
+        _require_cuda(t, nm)
+    batched = X.dim() == 3
+    if batched:
+        if packed.dim() != 3:
+            raise ValueError("X [L, M, K] needs packed [L, N, bytes]")
+        L, M, Kx = X.shape
+        N = packed.shape[1]
+        if packed.shape[0] != L or gamma.numel() != L:
+            raise ValueError("inconsistent batched shapes")
+    else:
+        if X.dim() != 2 or packed.dim() != 2:
+            raise ValueError("X must be [M, K] and packed [N, bytes]")
+        L = 1
+        M, Kx = X.shape
+        N = packed.shape[0]
+    K = Kx if K is None else K
+    if K != Kx:
+        raise ValueError("K does not match X")
+    if packed.shape[-1] != r3_row_bytes(K) or packed.element_size() != 1:
+        raise ValueError("packed does not hold r3_row_bytes(K) bytes per row")
+    lib = abi.load()
+    shape = (L, M, N) if batched else (M, N)
+    Y = out if out is not None else torch.empty(shape, dtype=torch.float32, device=X.device)
+    acc = torch.empty(shape, dtype=torch.int32, device=X.device) if return_acc else None
+    abi.check("bitlinear_forward_r3",
+              lib.bitlinear_forward_r3(L, _ptr(X), _x_dtype(X), M, K, _ptr(packed), N, _ptr(gamma),
+                                       _ptr(Y), _ptr(acc), _stream(X)))
+    return (Y, acc) if return_acc else Y

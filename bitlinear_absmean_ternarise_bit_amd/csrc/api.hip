@@ -35,6 +35,10 @@ bool decode_fits(int64_t M, int64_t K, int64_t N) {
   return M <= kDecodeMaxM && M * (padded_k(K) + 16) <= kDecodeMaxCodes && M * N < (int64_t(1) << 29);
 }
 
+bool decode_fits_r3(int64_t M, int64_t K, int64_t N) {
+  return M <= kDecodeMaxM && M * (r3_padded_k(K) + 16) <= kDecodeMaxCodes && M * N < (int64_t(1) << 29);
+}
+
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct PrefillWs {
@@ -167,6 +171,43 @@ int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, 
   if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(Y, 4)) return BITLINEAR_ERR_ALIGN;
   return hip_status(launch_decode(X, x_dtype, M, K, packed, N, gamma, Y, nullptr, L,
                                   static_cast<hipStream_t>(stream)));
+}
+
+int64_t bitlinear_r3_padded_k(int64_t K) { return K < 1 ? 0 : r3_padded_k(K); }
+
+size_t bitlinear_r3_packed_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(r3_padded_k(K)) / 5;
+}
+
+int bitlinear_quantize_weights_r3(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!W || !packed || !gamma) return BITLINEAR_ERR_NULL;
+  int st = check_mnk(1, N, K);
+  if (st) return st;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(gamma, 4)) return BITLINEAR_ERR_ALIGN;
+  if (!workspace || workspace_bytes < quantize_workspace_bytes()) return BITLINEAR_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return BITLINEAR_ERR_ALIGN;
+  return hip_status(launch_quantize_weights_r3(W, N, K, packed, gamma, workspace,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward_r3(int64_t L, const void* X, int x_dtype, int64_t M, int64_t K,
+                         const uint8_t* packed, int64_t N, const float* gamma, float* Y,
+                         int32_t* acc, void* stream) {
+  if (!X || !packed || !gamma || !Y) return BITLINEAR_ERR_NULL;
+  if (L < 1 || L > (int64_t(1) << 20)) return BITLINEAR_ERR_SHAPE;
+  int st = check_mnk(M, N, K);
+  if (st) return st;
+  st = check_x(X, x_dtype);
+  if (st) return st;
+  if (!decode_fits_r3(M, K, N)) return BITLINEAR_ERR_SHAPE;
+  const int64_t bpl = (N + 63) / 64;
+  if (L * bpl >= (int64_t(1) << 31)) return BITLINEAR_ERR_SHAPE;
+  if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(Y, 4) || (acc && !aligned(acc, 4)))
+    return BITLINEAR_ERR_ALIGN;
+  return hip_status(launch_decode_r3(X, x_dtype, M, K, packed, N, gamma, Y, acc, L,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 const char* bitlinear_status_string(int status) {

@@ -19,8 +19,23 @@
 // MFMA operands: for a 16x16x64 int8 MFMA lane l supplies 16 bytes of row
 // (l % 16) of A and of column (l % 16) of B, both for the same 16 k positions
 // (chosen by l / 16).  Here lane l feeds weight row n0 + l%16 from its own
-// packed word (16 weights = one B operand) and token l%16 from the same 16 k
-// of the LDS codes, so every k is paired consistently.
+// packed codes and token l%16 from the same 16 k of the LDS codes, so every k
+// is paired consistently.
+//
+// Two weight formats share the kernel; a row is a run of 16-byte units either
+// way:
+//   2-bit    a unit is 64 weights (four words of 16); one word unpacks with
+//            shifts and masks into one B operand, four MFMAs per unit;
+//   radix-3  a unit is 80 weights (four words of 20, five weights per byte,
+//            the Radix-3 packing of the article's bitnet.cpp section); byte b
+//            of word j holds k = 20j + 4t + b for t = 0..4 as
+//            ceil(256 v / 243) with v = sum_t c_t 3^(4-t).  Multiplying the
+//            byte by 3 puts digit t = 0 in bits 8-9 and the rest, which yields
+//            the next digit the same way, in bits 0-7.  Bytes 0,2 and 1,3 of
+//            a word are processed as two 16-bit lanes per register, so one
+//            multiply, one mask and half a byte permute give four codes.  The
+//            twenty code dwords of a unit, in (word, digit) order, are k = 4f
+//            .. 4f+3 of the unit: five B operands for five MFMAs.
 #include "kernels.hpp"
 #include "quant_act.hpp"
 
@@ -33,25 +48,73 @@ constexpr int kDecodeThreads = 256;
 constexpr int kWaves = kDecodeThreads / kWave;
 constexpr int kUnroll = 8;         // 16-byte loads per lane per batch (8 KiB per wave)
 
+// Radix-3 unpack of one word (20 weights): d[t] holds the offset codes of
+// k = 20j + 4t + b in byte b.
+__device__ __forceinline__ void unpack_r3_word(uint32_t w, int* d) {
+  uint32_t e = w & 0x00ff00ffu;         // bytes 0 and 2, one per 16-bit lane
+  uint32_t o = (w >> 8) & 0x00ff00ffu;  // bytes 1 and 3
+#pragma unroll
+  for (int t = 0; t < 5; ++t) {
+    e *= 3u;  // lane < 768: digit in bits 8-9 of the lane, rest in bits 0-7
+    o *= 3u;
+    // bytes {e.1, o.1, e.3, o.3}: the codes of bytes 0, 1, 2, 3 of the word
+    d[t] = static_cast<int>(__builtin_amdgcn_perm(o, e, 0x07030501u));
+    e &= 0x00ff00ffu;
+    o &= 0x00ff00ffu;
+  }
+}
+
+template <int FMT>
+struct Format;
+template <>
+struct Format<2> {
+  static constexpr int kPerUnit = 64;  // weights per 16-byte unit
+  static constexpr int kMfma = 4;      // MFMAs per unit
+};
+template <>
+struct Format<3> {
+  static constexpr int kPerUnit = 80;
+  static constexpr int kMfma = 5;
+};
+
+// B operands of one 16-byte unit, in k order.
+template <int FMT>
+__device__ __forceinline__ void unit_operands(const uint4& r, v4i (&bop)[Format<FMT>::kMfma]) {
+  const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+  if constexpr (FMT == 2) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) bop[t] = unpack_word(wd[t]);
+  } else {
+    int d[20];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) unpack_r3_word(wd[q], d + 5 * q);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) bop[i] = v4i{d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]};
+  }
+}
+
 // A wave owns `groups` blocks of 16 weight rows and walks them in batches of
-// kUnroll 16-word chunks; the loads of batch b+1 are issued before batch b is
-// contracted, and the first batch is in flight while phase A quantises X.
-template <int DT, bool VEC, bool WRITE_ACC>
+// kUnroll 16-byte loads per lane (each load instruction covers four
+// consecutive units of 16 rows); the loads of batch b+1 are issued before
+// batch b is contracted, and the first batch is in flight while phase A
+// quantises X.  Kp is the LDS row length in codes (units * kPerUnit).
+template <int FMT, int DT, bool VEC, bool WRITE_ACC>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
-    const void* __restrict__ X, int M, int64_t K, int64_t Kp, const uint32_t* __restrict__ packed,
-    int64_t N, const float* __restrict__ gamma, float* __restrict__ Y, int32_t* __restrict__ acc,
-    int blocks_per_layer, int groups) {
+    const void* __restrict__ X, int M, int64_t K, int64_t Kp, int64_t units,
+    const uint32_t* __restrict__ packed, int64_t N, const float* __restrict__ gamma,
+    float* __restrict__ Y, int32_t* __restrict__ acc, int blocks_per_layer, int groups) {
   extern __shared__ __align__(16) int8_t sxq[];
   __shared__ float s_ga[kDecodeMaxM];
   __shared__ int s_rs[kDecodeMaxM];
 
   constexpr int esize = DT == 0 ? 4 : 2;
+  constexpr int kPerUnit = Format<FMT>::kPerUnit;
+  constexpr int kMfma = Format<FMT>::kMfma;
   const int64_t layer = blockIdx.x / blocks_per_layer;
   const int rb = static_cast<int>(blockIdx.x - layer * blocks_per_layer);
-  const int64_t words = Kp >> 4;
   const int64_t lds_stride = Kp + 16;  // +16 bytes: token rows start on different banks
   X = static_cast<const char*>(X) + layer * M * K * esize;
-  packed += layer * N * words;
+  packed += layer * N * units * 4;
   Y += layer * M * N;
   if constexpr (WRITE_ACC) acc += layer * M * N;
   gamma += layer;
@@ -61,35 +124,35 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const int j = lane & 15;
   const int g = lane >> 4;
   const int64_t n_base = (static_cast<int64_t>(rb) * kWaves + wave) * groups * kRowsPerWave;
-  const int chunks = static_cast<int>((words + 15) >> 4);           // 16-word chunks per row
-  const int bpg = (chunks + kUnroll - 1) / kUnroll;                   // batches per row group
+  const int chunks = static_cast<int>((units + 3) >> 2);  // load instructions per row
+  const int bpg = (chunks + kUnroll - 1) / kUnroll;       // batches per row group
   const int nbatch = groups * bpg;
 
   // Packed rows are read, and outputs written, through buffer resources over
   // this layer's arrays.  Every load and store is unconditional: offsets that
-  // must not touch memory (rows past N, words past a row's end, batches past
+  // must not touch memory (rows past N, units past a row's end, batches past
   // the last, outputs that are not due yet) are set past the resource and the
   // hardware bounds check turns them into zeros / dropped stores.  Without
   // branches the compiler keeps the next batch of loads in flight while the
   // current one is contracted.
   constexpr uint32_t kOff = 0xfffffff0u;  // past every resource
   const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(packed), 0, static_cast<int>(N * words * 4), 0x00020000);
+      const_cast<uint32_t*>(packed), 0, static_cast<int>(N * units * 16), 0x00020000);
   const __amdgpu_buffer_rsrc_t ysrc = __builtin_amdgcn_make_buffer_rsrc(
       Y, 0, static_cast<int>(static_cast<int64_t>(M) * N * 4), 0x00020000);
   const __amdgpu_buffer_rsrc_t asrc = __builtin_amdgcn_make_buffer_rsrc(
       WRITE_ACC ? static_cast<void*>(acc) : static_cast<void*>(Y), 0,
       WRITE_ACC ? static_cast<int>(static_cast<int64_t>(M) * N * 4) : 0, 0x00020000);
-  const uint32_t words32 = static_cast<uint32_t>(words);
+  const uint32_t units32 = static_cast<uint32_t>(units);
   const uint32_t N32 = static_cast<uint32_t>(N);
   auto load_batch = [&](int b, bool valid, uint4 (&r)[kUnroll]) {
     const int gi = b / bpg;
     const int cb = b - gi * bpg;
-    const uint32_t row_off = static_cast<uint32_t>(n_base + gi * kRowsPerWave + j) * words32 * 4u;
+    const uint32_t row_off = static_cast<uint32_t>(n_base + gi * kRowsPerWave + j) * units32 * 16u;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t w0 = static_cast<uint32_t>(cb * kUnroll + u) * 16u + 4u * g;
-      const uint32_t off = (valid && w0 < words32) ? row_off + 4u * w0 : kOff;
+      const uint32_t un = static_cast<uint32_t>(cb * kUnroll + u) * 4u + g;
+      const uint32_t off = (valid && un < units32) ? row_off + 16u * un : kOff;
       const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off, 0, 0);
       r[u] = make_uint4(v[0], v[1], v[2], v[3]);
     }
@@ -112,8 +175,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   }
   __syncthreads();
 
-  const bool avalid = j < M;
-  const int8_t* arow = sxq + (avalid ? j : 0) * lds_stride;
+  // Lanes of tokens j >= M read token 0's codes: they only feed accumulator
+  // rows that are never stored.
+  const int8_t* arow = sxq + (j < M ? j : 0) * lds_stride;
   const v4i zero = {0, 0, 0, 0};
   const float gm = gamma[0];
   v4i c = zero;
@@ -123,15 +187,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const int cb = b - gi * bpg;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t w0 = static_cast<uint32_t>(cb * kUnroll + u) * 16u + 4u * g;
-      const bool use = avalid && w0 < words32;
-      const uint32_t wd[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+      const uint32_t un = static_cast<uint32_t>(cb * kUnroll + u) * 4u + g;
+      // units past the row end were loaded as zeros (all codes 0), so any
+      // in-bounds activation codes may pair with them
+      const uint32_t abase = un < units32 ? kPerUnit * un : 0u;
+      v4i bop[kMfma];
+      unit_operands<FMT>(r[u], bop);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const v4i bop = unpack_word(wd[t]);
-        const v4i araw = *reinterpret_cast<const v4i*>(arow + (use ? 16u * (w0 + t) : 0u));
-        const v4i a = use ? araw : zero;
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop, c, 0, 0, 0);
+      for (int t = 0; t < kMfma; ++t) {
+        const v4i a = *reinterpret_cast<const v4i*>(arow + abase + 16u * t);
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop[t], c, 0, 0, 0);
       }
     }
     // epilogue of the row group after its last batch: lane holds tokens
@@ -178,22 +243,36 @@ int pick_groups(int64_t L, int64_t N) {
   return 1;
 }
 
-template <int DT, bool VEC>
+template <int FMT, int DT, bool VEC>
 hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed, int64_t N,
                     const float* gamma, float* Y, int32_t* acc, int64_t L, hipStream_t stream) {
-  const int64_t Kp = padded_k(K);
+  const int64_t Kp = FMT == 2 ? padded_k(K) : r3_padded_k(K);
+  const int64_t units = Kp / Format<FMT>::kPerUnit;
   const int groups = pick_groups(L, N);
   const int64_t rows = int64_t(kWaves) * kRowsPerWave * groups;
   const int bpl = static_cast<int>((N + rows - 1) / rows);
   const int64_t blocks = L * bpl;
   const size_t lds = static_cast<size_t>(M) * static_cast<size_t>(Kp + 16);
   if (acc)
-    decode_kernel<DT, VEC, true><<<static_cast<unsigned>(blocks), kDecodeThreads, lds, stream>>>(
-        X, static_cast<int>(M), K, Kp, packed, N, gamma, Y, acc, bpl, groups);
+    decode_kernel<FMT, DT, VEC, true><<<static_cast<unsigned>(blocks), kDecodeThreads, lds, stream>>>(
+        X, static_cast<int>(M), K, Kp, units, packed, N, gamma, Y, acc, bpl, groups);
   else
-    decode_kernel<DT, VEC, false><<<static_cast<unsigned>(blocks), kDecodeThreads, lds, stream>>>(
-        X, static_cast<int>(M), K, Kp, packed, N, gamma, Y, acc, bpl, groups);
+    decode_kernel<FMT, DT, VEC, false><<<static_cast<unsigned>(blocks), kDecodeThreads, lds, stream>>>(
+        X, static_cast<int>(M), K, Kp, units, packed, N, gamma, Y, acc, bpl, groups);
   return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
+                      int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
+                      hipStream_t stream) {
+  const int esize = x_dtype == 0 ? 4 : 2;
+  const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ((K * esize) % 16 == 0);
+  if (x_dtype == 0)
+    return vec ? launch_v<FMT, 0, true>(X, M, K, packed, N, gamma, Y, acc, L, stream)
+               : launch_v<FMT, 0, false>(X, M, K, packed, N, gamma, Y, acc, L, stream);
+  return vec ? launch_v<FMT, 1, true>(X, M, K, packed, N, gamma, Y, acc, L, stream)
+             : launch_v<FMT, 1, false>(X, M, K, packed, N, gamma, Y, acc, L, stream);
 }
 
 }  // namespace
@@ -201,13 +280,14 @@ hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed,
 hipError_t launch_decode(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
                          int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
                          hipStream_t stream) {
-  const int esize = x_dtype == 0 ? 4 : 2;
-  const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ((K * esize) % 16 == 0);
-  if (x_dtype == 0)
-    return vec ? launch_v<0, true>(X, M, K, packed, N, gamma, Y, acc, L, stream)
-               : launch_v<0, false>(X, M, K, packed, N, gamma, Y, acc, L, stream);
-  return vec ? launch_v<1, true>(X, M, K, packed, N, gamma, Y, acc, L, stream)
-             : launch_v<1, false>(X, M, K, packed, N, gamma, Y, acc, L, stream);
+  return launch_fmt<2>(X, x_dtype, M, K, packed, N, gamma, Y, acc, L, stream);
+}
+
+hipError_t launch_decode_r3(const void* X, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
+                            int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
+                            hipStream_t stream) {
+  return launch_fmt<3>(X, x_dtype, M, K, reinterpret_cast<const uint32_t*>(packed), N, gamma, Y,
+                       acc, L, stream);
 }
 
 }  // namespace bitlinear

@@ -13,11 +13,16 @@ constexpr int kDecodeMaxM = 16;            // one MFMA row block of tokens
 constexpr int64_t kDecodeMaxCodes = 65536; // M * Kp int8 codes held in LDS
 
 inline int64_t padded_k(int64_t K) { return ((K + 63) / 64) * 64; }
+// radix-3 rows: a multiple of 80 weights (16 bytes)
+inline int64_t r3_padded_k(int64_t K) { return ((K + 79) / 80) * 80; }
 
 // a1 + a2
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_t* packed,
                                    float* gamma, void* workspace, hipStream_t stream);
 size_t quantize_workspace_bytes();
+// a1 + radix-3 pack (same workspace)
+hipError_t launch_quantize_weights_r3(const float* W, int64_t N, int64_t K, uint8_t* packed,
+                                      float* gamma, void* workspace, hipStream_t stream);
 
 // a3
 hipError_t launch_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, int8_t* Xq,
@@ -27,6 +32,11 @@ hipError_t launch_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, in
 hipError_t launch_decode(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
                          int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
                          hipStream_t stream);
+
+// a3 + a4 + a6 fused, radix-3 weights
+hipError_t launch_decode_r3(const void* X, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
+                            int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
+                            hipStream_t stream);
 
 // a5 + a6 (prefill): codes from launch_act_quant
 hipError_t launch_prefill_gemm(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum,

@@ -1,9 +1,11 @@
-// Offline weight quantisation: AbsMean scale, RoundClip ternary codes, 2-bit pack.
+// Offline weight quantisation: AbsMean scale, RoundClip ternary codes, and
+// either the 2-bit pack or the radix-3 pack (five weights per byte).
 //
 // [PMV] = produtoramaxvision.com.br article on BitNet b1.58 (ternary
 // quantisation, BitLinear, Zero-GEMM).  gamma = (1/(n m)) sum |W_ij| and
 // W_q = Round(Clip(W / (gamma + eps), -1, 1)) are its section-1 AbsMean
-// equations; 2 bits per weight is its section-3 packing.
+// equations; 2 bits per weight is its section-3 packing; five weights per
+// byte (3^5 = 243 <= 256) is the Radix-3 packing of its section on bitnet.cpp.
 //
 // gamma is computed exactly and order-independently: each |w| is an integer
 // significand times a power of two, so the sum is an integer in units of
@@ -189,6 +191,15 @@ __global__ __launch_bounds__(256) void absmean_finalize_kernel(const unsigned lo
   gamma[0] = static_cast<float>(sum / count);
 }
 
+// Offset code c = q + 1 of one weight, q = Round(Clip(w / d, -1, 1)) with an
+// IEEE float32 division and round half to even; padding (valid false) is a
+// zero weight, c = 1.
+__device__ __forceinline__ uint32_t offset_code(float w, float d, bool valid) {
+  const float t = __fdiv_rn(w, d);
+  const float q = __builtin_rintf(fminf(fmaxf(t, -1.0f), 1.0f));
+  return valid ? static_cast<uint32_t>(static_cast<int>(q) + 1) : 1u;
+}
+
 // Ternarise and pack.  Each lane turns four consecutive weights (k = 4f..4f+3)
 // into the four bytes' bit pair 2i of word f/4 (i = f%4); four adjacent lanes
 // OR their parts into one word.
@@ -215,15 +226,7 @@ __global__ __launch_bounds__(256) void ternarise_pack_kernel(const float* __rest
     }
     uint32_t part = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      uint32_t c = 1u;  // padding: zero weight
-      if (kq + b < K) {
-        const float t = __fdiv_rn(w[b], d);
-        const float q = __builtin_rintf(fminf(fmaxf(t, -1.0f), 1.0f));
-        c = static_cast<uint32_t>(static_cast<int>(q) + 1);
-      }
-      part |= c << (8 * b);
-    }
+    for (int b = 0; b < 4; ++b) part |= offset_code(w[b], d, kq + b < K) << (8 * b);
     const int i = static_cast<int>(f & 3);
     part <<= 2 * i;
     part |= __shfl_xor(part, 1, 4);
@@ -232,16 +235,74 @@ __global__ __launch_bounds__(256) void ternarise_pack_kernel(const float* __rest
   }
 }
 
-}  // namespace
+// Ternarise and pack five weights per byte.  One lane writes one 32-bit word
+// of a row: 20 weights k = 20j + 4t + b (byte b, digit t).  Byte b holds
+// v = sum_t c_t 3^(4-t) as ceil(256 v / 243), so a decoder reads the digits
+// most significant first by repeated multiplication by three.
+template <bool VEC>
+__global__ __launch_bounds__(256) void ternarise_pack_r3_kernel(const float* __restrict__ W, int64_t N,
+                                                                int64_t K, int64_t words_per_row,
+                                                                const float* __restrict__ gamma,
+                                                                uint32_t* __restrict__ packed) {
+  const float d = __fadd_rn(gamma[0], kEps);
+  const int64_t total = N * words_per_row;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t f = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; f < total; f += stride) {
+    const int64_t n = f / words_per_row;
+    const int64_t k0 = (f - n * words_per_row) * 20;
+    const float* row = W + n * K;
+    uint32_t v[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < 5; ++t) {
+      const int64_t k = k0 + 4 * t;
+      float w[4];
+      if (VEC && k + 3 < K) {
+        const float4 x = *reinterpret_cast<const float4*>(row + k);
+        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) w[b] = (k + b < K) ? row[k + b] : 0.0f;
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v[b] = 3u * v[b] + offset_code(w[b], d, k + b < K);
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) word |= ((256u * v[b] + 242u) / 243u) << (8 * b);
+    packed[f] = word;
+  }
+}
 
-hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_t* packed,
-                                   float* gamma, void* workspace, hipStream_t stream) {
+void launch_gamma(const float* W, int64_t N, int64_t K, float* gamma, void* workspace,
+                  hipStream_t stream) {
   const uint64_t n = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
   auto* partial = static_cast<unsigned long long*>(workspace);
   const uint64_t want = (n / 4 + 255) / 256;
   const int blocks = static_cast<int>(want < 1 ? 1 : (want > kAbsmeanBlocks ? kAbsmeanBlocks : want));
   absmean_digits_kernel<<<blocks, 256, 0, stream>>>(W, n, partial);
   absmean_finalize_kernel<<<1, 256, 0, stream>>>(partial, blocks, static_cast<double>(n), gamma);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_weights_r3(const float* W, int64_t N, int64_t K, uint8_t* packed,
+                                      float* gamma, void* workspace, hipStream_t stream) {
+  launch_gamma(W, N, K, gamma, workspace, stream);
+  const int64_t wpr = r3_padded_k(K) / 20;
+  const int64_t total = N * wpr;
+  int64_t pblocks = (total + 255) / 256;
+  if (pblocks > 65536) pblocks = 65536;
+  uint32_t* out = reinterpret_cast<uint32_t*>(packed);
+  if ((K & 3) == 0)
+    ternarise_pack_r3_kernel<true><<<static_cast<int>(pblocks), 256, 0, stream>>>(W, N, K, wpr, gamma, out);
+  else
+    ternarise_pack_r3_kernel<false><<<static_cast<int>(pblocks), 256, 0, stream>>>(W, N, K, wpr, gamma, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_t* packed,
+                                   float* gamma, void* workspace, hipStream_t stream) {
+  launch_gamma(W, N, K, gamma, workspace, stream);
   const int64_t Kp = padded_k(K);
   const int64_t total = N * (Kp / 4);
   int64_t pblocks = (total + 255) / 256;

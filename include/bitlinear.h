@@ -6,7 +6,9 @@
  * section on why ternary weights carry 1.58 bits (AbsMean and AbsMax
  * equations), [PMV s2] the section on how BitLinear removes multiplications
  * (add/subtract/skip, INT32 accumulation, rescale by gamma_A * gamma / 127),
- * [PMV s3] the section on the memory wall (2-bit packing, 0.25 byte/weight).
+ * [PMV s3] the section on the memory wall (2-bit packing, 0.25 byte/weight),
+ * [PMV s4] the section on how bitnet.cpp speeds up inference on CPUs (the
+ * LUT figure and the Radix-3 packing of five weights per byte).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -23,8 +25,8 @@
  *  - Sizes: 1 <= M, N, K; N*K < 2^32; M*N < 2^40; K <= 2^20.
  *  - Non-finite inputs (inf/nan in W or X) give unspecified results.
  *
- * Packed ternary weights (the format of `packed` everywhere)
- * ----------------------------------------------------------
+ * Packed ternary weights (the format of `packed` outside the radix-3 calls)
+ * -------------------------------------------------------------------------
  * Each weight is stored as a 2-bit code c = q + 1 in {0,1,2} (3 never occurs),
  * [PMV s3].  A row of K weights is padded to Kp = bitlinear_padded_k(K) (a
  * multiple of 64) with c = 1, i.e. zero weights, and stored as Kp/16
@@ -189,6 +191,53 @@ int bitlinear_forward_quantized(const int8_t* Xq, const float* gamma_a, const in
 int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, int64_t K,
                               const uint32_t* packed, int64_t N, const float* gamma,
                               float* Y, void* stream);
+
+/* ---- radix-3 weights: five per byte ------------------------------------ */
+/*
+ * The Radix-3 packing of [PMV s4] (the section on how bitnet.cpp speeds up CPU
+ * inference): five ternary weights per byte since 3^5 = 243 <= 256, 1.60 bits
+ * per weight, 20% fewer weight bytes than the 2-bit format for the
+ * bandwidth-bound decode path.  The section's LUT figure indexes a group of
+ * weights as a base-3 number of the offset digits c = q + 1.
+ *
+ * Format (this library's own; the article fixes only the count): a row of K
+ * weights is padded with c = 1 to Kp3 = bitlinear_r3_padded_k(K), a multiple
+ * of 80, and stored as Kp3/5 bytes; rows follow each other with no gap.  Byte
+ * 4j + b of a row (b = 0..3) holds the five weights k = 20j + 4t + b,
+ * t = 0..4, as ceil(256 * v / 243) with v = sum_t c_t * 3^(4 - t).  13 byte
+ * values never occur.  The buffer carries no header.
+ */
+
+/* Kp3: K rounded up to a multiple of 80. */
+int64_t bitlinear_r3_padded_k(int64_t K);
+
+/* Bytes of a radix-3 packed [N, K] matrix: N * Kp3 / 5. */
+size_t bitlinear_r3_packed_bytes(int64_t N, int64_t K);
+
+/*
+ * bitlinear_quantize_weights with the radix-3 format: the same gamma and the
+ * same ternary codes (bit-identical), packed five per byte.
+ * packed: device, bitlinear_r3_packed_bytes(N, K) bytes, 16-byte aligned.
+ * Other arguments and the workspace as for bitlinear_quantize_weights.
+ */
+int bitlinear_quantize_weights_r3(const float* W, int64_t N, int64_t K,
+                                  uint8_t* packed, float* gamma,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode forward(s) over radix-3 weights: for l = 0..L-1,
+ *   Y_l = (Xq_l x q_l^T) * gamma[l] * gamma_A / 127              [PMV s2]
+ * with the same fused kernel as the 2-bit decode path (token codes in on-chip
+ * memory, weights streamed once).  Layer l reads X + l*M*K elements,
+ * packed + l*bitlinear_r3_packed_bytes(N, K) bytes and gamma[l], and writes
+ * Y + l*M*N (and acc + l*M*N when acc is not NULL: the exact INT32
+ * accumulators).  Requires M <= bitlinear_max_decode_m(),
+ * M*(Kp3+16) <= bitlinear_max_decode_codes() and M*N < 2^29;
+ * packed 16-byte aligned, Y and acc 4-byte aligned.
+ */
+int bitlinear_forward_r3(int64_t L, const void* X, int x_dtype, int64_t M, int64_t K,
+                         const uint8_t* packed, int64_t N, const float* gamma,
+                         float* Y, int32_t* acc, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* bitlinear_status_string(int status);

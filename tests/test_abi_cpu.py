@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(abi.SIGNATURES)
@@ -51,6 +51,37 @@ def test_sizes(lib):
     assert lib.bitlinear_forward_workspace_bytes(10, 100) % 256 == 0
     assert lib.bitlinear_max_decode_m() == 16
     assert lib.bitlinear_max_decode_codes() == 65536
+
+
+def test_r3_sizes(lib):
+    assert lib.bitlinear_r3_padded_k(1) == 80
+    assert lib.bitlinear_r3_padded_k(80) == 80
+    assert lib.bitlinear_r3_padded_k(81) == 160
+    assert lib.bitlinear_r3_padded_k(0) == 0
+    assert lib.bitlinear_r3_packed_bytes(2048, 2080) == 2048 * 2080 // 5  # 1.6 bits per weight
+    assert lib.bitlinear_r3_packed_bytes(3, 100) == 3 * 160 // 5
+    assert lib.bitlinear_r3_packed_bytes(5, 0) == 0
+
+
+def test_r3_checks(lib):
+    ws = lib.bitlinear_quantize_workspace_bytes()
+    f = lib.bitlinear_quantize_weights_r3
+    assert f(None, 4, 4, FAKE, FAKE, FAKE, ws, None) == abi.ERR_NULL
+    assert f(FAKE, 4, 4, None, FAKE, FAKE, ws, None) == abi.ERR_NULL
+    assert f(FAKE, 0, 4, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE
+    assert f(FAKE, 1 << 13, 1 << 19, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE
+    assert f(FAKE, 4, 4, P(4104), FAKE, FAKE, ws, None) == abi.ERR_ALIGN
+    assert f(FAKE, 4, 4, FAKE, FAKE, FAKE, ws - 1, None) == abi.ERR_WORKSPACE
+    g = lib.bitlinear_forward_r3
+    #   L, X, dt, M, K, packed, N, gamma, Y, acc, stream
+    assert g(1, None, 0, 1, 64, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_NULL
+    assert g(1, FAKE, 0, 1, 64, FAKE, 8, FAKE, None, None, None) == abi.ERR_NULL
+    assert g(0, FAKE, 0, 1, 64, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_SHAPE
+    assert g(1, FAKE, 0, 17, 64, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_SHAPE   # M > 16
+    assert g(1, FAKE, 0, 16, 4081, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_SHAPE  # codes > LDS
+    assert g(1, FAKE, 2, 1, 64, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_DTYPE
+    assert g(1, FAKE, 0, 1, 64, P(4104), 8, FAKE, FAKE, None, None) == abi.ERR_ALIGN
+    assert g(1, FAKE, 0, 1, 64, FAKE, 8, FAKE, FAKE, P(4098), None) == abi.ERR_ALIGN
 
 
 def test_status_strings(lib):

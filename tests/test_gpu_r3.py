@@ -1,0 +1,178 @@
+"""Radix-3 weights (five per byte) on the GPU, through the C ABI, against the oracle.
+
+Bit-exact: gamma, the packed bytes and the INT32 accumulators; Y within
+|Y - Y_ref| <= 1e-5 |Y_ref|.  The radix-3 forward must also equal the 2-bit
+decode forward bit for bit (same codes, same epilogue).
+"""
+import numpy as np
+import pytest
+import torch
+
+import bitlinear_absmean_ternarise_bit_amd as bl
+import oracle as O
+from bitlinear_absmean_ternarise_bit_amd import abi
+from bitlinear_absmean_ternarise_bit_amd.workloads import make_workload, random_problem
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+RTOL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev_x(P):
+    if P.x_dtype == "bf16":
+        return torch.from_numpy(P.X_bf16_bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(P.X).to(DEV)
+
+
+def check_y(y, yr):
+    y = np.asarray(y, dtype=np.float64)
+    yr = np.asarray(yr, dtype=np.float64)
+    ok = np.abs(y - yr) <= RTOL * np.abs(yr)
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        raise AssertionError(f"Y mismatch at {idx.tolist()}: gpu {y[tuple(idx.T)]} ref {yr[tuple(idx.T)]}")
+
+
+def test_sizes_match_oracle():
+    for K in (1, 79, 80, 81, 2048, 5632, 8192):
+        assert bl.r3_padded_k(K) == O.r3_padded_k(K)
+        assert abi.load().bitlinear_r3_packed_bytes(7, K) == O.r3_packed_bytes(7, K)
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (3, 19), (5, 79), (70, 80), (33, 81), (257, 1000), (64, 2048),
+                                 (2050, 333), (16, 4097)])
+def test_quantize_weights_r3_bit_exact(N, K):
+    say(f"quantize_weights_r3 N={N} K={K}")
+    P = random_problem(1, K, N, seed=3 * N + K)
+    W = torch.from_numpy(P.W).to(DEV)
+    p3, g3 = bl.quantize_weights_r3(W)
+    p2, g2 = bl.quantize_weights(W)
+    torch.cuda.synchronize()
+    g, q, _ = O.quantize_weights(P.W)
+    assert g3.item() == float(g) == g2.item()
+    assert np.array_equal(p3.cpu().numpy(), O.pack_codes_r3(q))
+
+
+def test_quantize_weights_r3_ties_and_zero_matrix():
+    W = np.full((40, 170), 0.01, np.float32)
+    for _ in range(20):  # entries at exactly half of gamma + eps round to 0 (half to even)
+        d = np.float32(O.absmean_gamma(W) + O.EPS32)
+        W[:, :8] = np.float32(d * np.float32(0.5)) * np.array([1, -1] * 4, np.float32)
+    for w in (W, np.zeros((9, 90), np.float32)):
+        p3, g3 = bl.quantize_weights_r3(torch.from_numpy(w).to(DEV))
+        torch.cuda.synchronize()
+        g, q, _ = O.quantize_weights(w)
+        assert g3.item() == float(g)
+        assert np.array_equal(p3.cpu().numpy(), O.pack_codes_r3(q))
+
+
+R3_CASES = [
+    (1, 1, 1, "f32"),
+    (1, 80, 16, "bf16"),
+    (3, 81, 70, "f32"),
+    (16, 300, 129, "bf16"),
+    (5, 1001, 1000, "bf16"),     # odd K: 2-byte X loads
+    (8, 2048, 5632, "bf16"),
+    (1, 4096, 2050, "f32"),
+    (2, 8191, 300, "f32"),
+    (1, 20000, 64, "bf16"),      # long rows: several batches per row group
+    (16, 4080, 100, "bf16"),     # the largest token block that fits on chip
+]
+
+
+@pytest.mark.parametrize("M,K,N,dt", R3_CASES)
+def test_forward_r3_parity(M, K, N, dt):
+    say(f"forward_r3 M={M} K={K} N={N} {dt}")
+    P = random_problem(M, K, N, seed=M + 5 * K + 11 * N, x_dtype=dt)
+    W = torch.from_numpy(P.W).to(DEV)
+    X = dev_x(P)
+    p3, g3 = bl.quantize_weights_r3(W)
+    Y, acc = bl.forward_r3(X, p3, g3, K, return_acc=True)
+    p2, g2 = bl.quantize_weights(W)
+    Y2, acc2 = bl.forward(X, p2, g2, K, return_acc=True)  # decode where it fits, else prefill
+    torch.cuda.synchronize()
+    ref = O.bitlinear_forward(P.X, P.W)
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    check_y(Y.cpu().numpy(), ref["Y"])
+    assert torch.equal(acc, acc2) and torch.equal(Y, Y2)
+
+
+def test_forward_r3_from_oracle_packed_bytes():
+    # the decoder alone: bytes packed by the oracle, not by the GPU packer
+    M, K, N = 4, 1234, 150
+    rng = np.random.default_rng(17)
+    q = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    P = random_problem(M, K, N, seed=17, x_dtype="bf16")
+    packed = torch.from_numpy(O.pack_codes_r3(q)).to(DEV)
+    gamma = torch.tensor([0.0375], dtype=torch.float32, device=DEV)
+    Y, acc = bl.forward_r3(dev_x(P), packed, gamma, K, return_acc=True)
+    torch.cuda.synchronize()
+    ref = O.forward_from_codes(P.X, q, np.float32(0.0375))
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    check_y(Y.cpu().numpy(), ref["Y"])
+
+
+def test_worked_example_r3():
+    # the article's Zero-GEMM example (acc = -149) through the radix-3 path
+    x = np.array([[42, -18, 105, -7, 88, 12, -64, 3, 127]], np.float32)
+    w = np.array([[1, 0, -1, 1, 0, -1, 1, -1, 0]], np.float32) * np.float32(0.02)
+    p3, g3 = bl.quantize_weights_r3(torch.from_numpy(w).to(DEV))
+    Y, acc = bl.forward_r3(torch.from_numpy(x).to(DEV), p3, g3, 9, return_acc=True)
+    torch.cuda.synchronize()
+    assert acc.item() == -149
+    assert Y.item() == float(np.float32(-149.0 * float(O.absmean_gamma(w))))
+
+
+def test_forward_r3_batched_layers():
+    L, M, K, N = 6, 3, 700, 210
+    Ps = [random_problem(M, K, N, seed=300 + l, x_dtype="bf16") for l in range(L)]
+    X = torch.stack([dev_x(P) for P in Ps])
+    q = [bl.quantize_weights_r3(torch.from_numpy(P.W).to(DEV)) for P in Ps]
+    packed = torch.stack([p for p, _ in q])
+    gamma = torch.cat([g for _, g in q])
+    Yb, accb = bl.forward_r3(X, packed, gamma, K, return_acc=True)
+    torch.cuda.synchronize()
+    for l, P in enumerate(Ps):
+        ref = O.bitlinear_forward(P.X, P.W)
+        assert np.array_equal(accb[l].cpu().numpy(), ref["acc"])
+        check_y(Yb[l].cpu().numpy(), ref["Y"])
+
+
+def test_forward_r3_limits():
+    lib = abi.load()
+    K = 4081  # Kp3 = 4160: 16 * (4160 + 16) > 65536, while K = 4080 fits exactly
+    assert not bl.r3_decode_fits(16, K, 10) and bl.r3_decode_fits(16, 4080, 10)
+    X = torch.zeros((16, K), dtype=torch.float32, device=DEV)
+    packed = torch.zeros((10, bl.r3_row_bytes(K)), dtype=torch.uint8, device=DEV)
+    gamma = torch.ones((1,), dtype=torch.float32, device=DEV)
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.forward_r3(X, packed, gamma, K)
+    assert e.value.status == abi.ERR_SHAPE
+    X17 = torch.zeros((17, 64), dtype=torch.float32, device=DEV)
+    p17 = torch.zeros((10, bl.r3_row_bytes(64)), dtype=torch.uint8, device=DEV)
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.forward_r3(X17, p17, gamma, 64)
+    assert e.value.status == abi.ERR_SHAPE
+    assert lib.bitlinear_forward_r3(0, X.data_ptr(), 0, 1, 64, packed.data_ptr(), 10, gamma.data_ptr(),
+                                    X.data_ptr(), None, None) == abi.ERR_SHAPE
+
+
+@pytest.mark.parametrize("name", ["single_m4_k256_n128", "decode_m1_k2048_n2048",
+                                  "decode_ffn_up_m8_k2048_n5632"])
+def test_workload_full_r3(name):
+    say(f"workload {name} radix-3")
+    P = make_workload(name)
+    W = torch.from_numpy(P.W).to(DEV)
+    p3, g3 = bl.quantize_weights_r3(W)
+    Y, acc = bl.forward_r3(dev_x(P), p3, g3, P.K, return_acc=True)
+    torch.cuda.synchronize()
+    ref = O.bitlinear_forward(P.X, P.W)
+    assert g3.item() == float(ref["gamma"])
+    assert np.array_equal(p3.cpu().numpy(), O.pack_codes_r3(ref["q"]))
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    check_y(Y.cpu().numpy(), ref["Y"])
