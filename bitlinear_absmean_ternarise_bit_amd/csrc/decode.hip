@@ -46,13 +46,12 @@ namespace {
 constexpr int kRowsPerWave = 16;   // one MFMA column block of weight rows
 constexpr int kDecodeThreads = 256;
 constexpr int kWaves = kDecodeThreads / kWave;
-constexpr int kUnroll = 8;         // 16-byte loads per lane per batch (8 KiB per wave)
 
 // Radix-3 unpack of one word (20 weights): d[t] holds the offset codes of
 // k = 20j + 4t + b in byte b.
 __device__ __forceinline__ void unpack_r3_word(uint32_t w, int* d) {
-  uint32_t e = w & 0x00ff00ffu;         // bytes 0 and 2, one per 16-bit lane
-  uint32_t o = (w >> 8) & 0x00ff00ffu;  // bytes 1 and 3
+  uint32_t e = w & 0x00ff00ffu;                             // bytes 0 and 2, one per 16-bit lane
+  uint32_t o = __builtin_amdgcn_perm(w, w, 0x0c030c01u);    // bytes 1 and 3 (selector 12 gives 0)
 #pragma unroll
   for (int t = 0; t < 5; ++t) {
     e *= 3u;  // lane < 768: digit in bits 8-9 of the lane, rest in bits 0-7
@@ -70,14 +69,19 @@ template <>
 struct Format<2> {
   static constexpr int kPerUnit = 64;  // weights per 16-byte unit
   static constexpr int kMfma = 4;      // MFMAs per unit
+  static constexpr int kUnroll = 8;    // 16-byte loads per lane per batch (8 KiB per wave)
 };
 template <>
 struct Format<3> {
   static constexpr int kPerUnit = 80;
   static constexpr int kMfma = 5;
+  // 7 loads per batch: rows of 2048 and 11008 weights (26 and 138 units, 7
+  // and 35 load instructions) fill their batches exactly
+  static constexpr int kUnroll = 7;
 };
 
-// B operands of one 16-byte unit, in k order.
+// B operands of one 16-byte unit, in k order.  Unit slots past a row's end
+// were loaded as zero bytes, which decode to all-zero operands in both formats.
 template <int FMT>
 __device__ __forceinline__ void unit_operands(const uint4& r, v4i (&bop)[Format<FMT>::kMfma]) {
   const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
@@ -110,6 +114,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   constexpr int esize = DT == 0 ? 4 : 2;
   constexpr int kPerUnit = Format<FMT>::kPerUnit;
   constexpr int kMfma = Format<FMT>::kMfma;
+  constexpr int kUnroll = Format<FMT>::kUnroll;
   const int64_t layer = blockIdx.x / blocks_per_layer;
   const int rb = static_cast<int>(blockIdx.x - layer * blocks_per_layer);
   const int64_t lds_stride = Kp + 16;  // +16 bytes: token rows start on different banks
@@ -188,8 +193,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint32_t un = static_cast<uint32_t>(cb * kUnroll + u) * 4u + g;
-      // units past the row end were loaded as zeros (all codes 0), so any
-      // in-bounds activation codes may pair with them
+      // units past the row end give all-zero operands, so any in-bounds
+      // activation codes may pair with them
       const uint32_t abase = un < units32 ? kPerUnit * un : 0u;
       v4i bop[kMfma];
       unit_operands<FMT>(r[u], bop);
