@@ -9,5 +9,6 @@ from .bitlinear_oracle import (EPS32, absmax_quantize, absmean_gamma, absmean_ga
                                forward_from_codes, pack_codes, padded_k, quantize_weights,
                                sampled_forward, ternary_codes, unpack_codes, zero_gemm,
                                zero_gemm_dot, zero_gemm_naive)
+from .bitlinear_oracle import deinterleave_units, interleave_units
 from .bitlinear_oracle import (R3_UNIT, pack_codes_r3, r3_byte, r3_packed_bytes, r3_padded_k,
                                r3_value, r3_value_of_byte, unpack_codes_r3)

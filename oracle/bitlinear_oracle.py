@@ -42,6 +42,9 @@ Readings where the article leaves a step open:
   multiple of 64 weights with c = 1 (a zero weight); row n is a run of
   little-endian 32-bit words, word j covers k in [16j, 16j + 16), and bits
   [8b + 2i, 8b + 2i + 1] of word j hold the code of k = 16j + 4i + b.
+* Both packed formats (2-bit and radix-3) cut each row into 16-byte units and
+  store the units of 16 consecutive rows interleaved: see
+  :func:`interleave_units`.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against the article's worked example, brute force, ``math.fsum``, closed forms
@@ -136,10 +139,61 @@ def padded_k(K: int) -> int:
     return ((K + PAD_MULTIPLE - 1) // PAD_MULTIPLE) * PAD_MULTIPLE
 
 
+# ---------------------------------------------------------------------------
+# Memory order of packed rows (this library's layout; the article fixes only
+# the bits per weight).  A packed row is a run of U 16-byte units.  Rows are
+# taken in blocks of 16 consecutive rows (the last block holds the N % 16 rows
+# left over, if any) and a block's units in chunks of 4 consecutive units (the
+# last chunk holds the U % 4 units left over, if any).  Blocks follow each
+# other; within a block the chunks follow each other; within a chunk each row
+# of the block, in order, stores its units of that chunk contiguously.  So 16
+# full rows x 4 units make one contiguous 1 KiB piece, and a row block takes
+# as many bytes as the same rows stored one after another.
+# ---------------------------------------------------------------------------
+
+ROW_BLOCK = 16
+UNIT_CHUNK = 4
+
+
+def interleave_units(rows: np.ndarray) -> np.ndarray:
+    """Row-major units [N, U, 16] (uint8) -> the packed buffer as flat uint8, in memory order."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    N, U, sixteen = rows.shape
+    assert sixteen == 16
+    out = []
+    for b0 in range(0, N, ROW_BLOCK):
+        R = min(ROW_BLOCK, N - b0)
+        for c0 in range(0, U, UNIT_CHUNK):
+            W = min(UNIT_CHUNK, U - c0)
+            for j in range(R):
+                out.append(rows[b0 + j, c0:c0 + W].reshape(-1))
+    return np.concatenate(out) if out else np.zeros(0, np.uint8)
+
+
+def deinterleave_units(flat: np.ndarray, N: int, U: int) -> np.ndarray:
+    """Inverse of :func:`interleave_units`: flat uint8 buffer -> units [N, U, 16]."""
+    flat = np.asarray(flat, dtype=np.uint8).reshape(-1)
+    if flat.size != N * U * 16:
+        raise ValueError("deinterleave_units: buffer size does not match N x U units")
+    rows = np.empty((N, U, 16), dtype=np.uint8)
+    pos = 0
+    for b0 in range(0, N, ROW_BLOCK):
+        R = min(ROW_BLOCK, N - b0)
+        for c0 in range(0, U, UNIT_CHUNK):
+            W = min(UNIT_CHUNK, U - c0)
+            for j in range(R):
+                rows[b0 + j, c0:c0 + W] = flat[pos:pos + 16 * W].reshape(W, 16)
+                pos += 16 * W
+    return rows
+
+
 def pack_codes(q: np.ndarray) -> np.ndarray:
     """Pack ternary codes [N, K] into uint32 words [N, padded_k(K) // 16].
 
-    Layout: see the module docstring.  0.25 byte per weight  [PMV §3].
+    Layout: see the module docstring; the returned array's memory order is
+    the packed buffer (rows interleaved by :func:`interleave_units`), so only
+    for N = 1 is row n of the array row n of the matrix.  0.25 byte per
+    weight  [PMV §3].
     """
     q = np.asarray(q)
     N, K = q.shape
@@ -151,13 +205,19 @@ def pack_codes(q: np.ndarray) -> np.ndarray:
     for i in range(4):
         for b in range(4):
             words |= c[:, :, i, b] << np.uint32(8 * b + 2 * i)
-    return words
+    # memory order: 16-byte units (four words) of 16-row blocks interleaved
+    units = words.astype('<u4').view(np.uint8).reshape(N, Kp // 64, 16)
+    return interleave_units(units).view('<u4').reshape(N, Kp // 16)
 
 
 def unpack_codes(words: np.ndarray, K: int) -> np.ndarray:
     """Inverse of :func:`pack_codes`; returns int8 codes [N, K] (raises on field value 3)."""
     words = np.asarray(words, dtype=np.uint32)
     N, nw = words.shape
+    if nw % 4:
+        raise ValueError("unpack_codes: rows are not whole 16-byte units")
+    units = deinterleave_units(words.astype('<u4').view(np.uint8), N, nw // 4)
+    words = units.reshape(N, nw * 4).view('<u4').astype(np.uint32)
     out = np.empty((N, nw, 4, 4), dtype=np.int64)
     for i in range(4):
         for b in range(4):
@@ -185,7 +245,8 @@ def unpack_codes(words: np.ndarray, K: int) -> np.ndarray:
 #   multiplying the byte, as a fraction of 256, by three;
 # * a row of K weights is padded with c = 1 (zero weights) to a multiple of 80;
 #   byte 4j + b of a row (b = 0..3) holds the weights k = 20j + 4t + b for
-#   t = 0..4, so 16-byte pieces of a row cover 80 consecutive weights.
+#   t = 0..4, so 16-byte units of a row cover 80 consecutive weights; rows are
+#   interleaved in memory like the 2-bit format's (:func:`interleave_units`).
 
 R3_UNIT = 80  # weights per 16 bytes of a radix-3 row
 R3_DIGITS = 5
@@ -236,16 +297,17 @@ def pack_codes_r3(q: np.ndarray) -> np.ndarray:
     for t in range(R3_DIGITS):
         v = 3 * v + c[:, :, t, :]
     out = (256 * v + 242) // 243
-    return out.reshape(N, Kp // R3_DIGITS).astype(np.uint8)
+    units = out.reshape(N, Kp // R3_UNIT, 16).astype(np.uint8)
+    return interleave_units(units).reshape(N, Kp // R3_DIGITS)
 
 
 def unpack_codes_r3(packed: np.ndarray, K: int) -> np.ndarray:
     """Inverse of :func:`pack_codes_r3`; int8 codes [N, K] (raises on a byte that encodes nothing)."""
     packed = np.asarray(packed, dtype=np.uint8)
     N, nb = packed.shape
-    if nb % 4:
-        raise ValueError("unpack_codes_r3: row length is not a whole number of 4-byte words")
-    b = packed.astype(np.int64)
+    if nb % 16:
+        raise ValueError("unpack_codes_r3: rows are not whole 16-byte units")
+    b = deinterleave_units(packed, N, nb // 16).reshape(N, nb).astype(np.int64)
     v = (243 * b) >> 8
     if np.any((256 * v + 242) // 243 != b):
         raise ValueError("unpack_codes_r3: byte that is not a radix-3 encoding")
