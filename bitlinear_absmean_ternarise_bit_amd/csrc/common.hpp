@@ -42,6 +42,20 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
+// Byte offset of 16-byte unit u of row n in a packed matrix of N rows of U
+// units.  Rows are stored in blocks of 16 (the last block holds N % 16 rows
+// if that is not 0) and a block's units in chunks of 4 (the last chunk holds
+// U % 4 units if that is not 0); within a chunk each row of the block stores
+// its units of the chunk contiguously.  A full chunk is 16 rows x 64 bytes in
+// one contiguous KiB, and a block takes as many bytes as its rows stored one
+// after another.  Requires n < N and u < U.
+__device__ __forceinline__ uint32_t unit_offset(uint32_t n, uint32_t u, uint32_t N, uint32_t U) {
+  const uint32_t b = n >> 4, j = n & 15u, c = u >> 2, g = u & 3u;
+  const uint32_t R = min(16u, N - 16u * b);
+  const uint32_t W = min(4u, U - 4u * c);
+  return (16u * b * U + c * R * 4u + j * W + g) * 16u;
+}
+
 // Four 2-bit codes per byte lane: (word >> 2i) & 0x03030303 gives the int8
 // codes of k = 16j + 4i .. 16j + 4i + 3, so the four results are the sixteen
 // codes of a packed word in k order.

@@ -3,9 +3,10 @@
 //   phase A  each workgroup quantises the (few) tokens into LDS with the
 //            per-token AbsMax quantiser (one wave per token);
 //   phase B  each wave streams the packed codes of 16 weight rows once from
-//            HBM (16 bytes per lane per load, 64 contiguous bytes per row per
-//            load instruction), unpacks them in registers and contracts them
-//            against the LDS codes with v_mfma_i32_16x16x64_i8;
+//            HBM (16 bytes per lane per load; the rows' interleaved order
+//            makes one load instruction one contiguous KiB), unpacks them in
+//            registers and contracts them against the LDS codes with
+//            v_mfma_i32_16x16x64_i8;
 //   epilogue INT32 accumulator -> float32 times gamma * gamma_A / 127.
 //
 // [PMV] = produtoramaxvision.com.br article on BitNet b1.58: section 2's
@@ -46,6 +47,7 @@ namespace {
 constexpr int kRowsPerWave = 16;   // one MFMA column block of weight rows
 constexpr int kDecodeThreads = 256;
 constexpr int kWaves = kDecodeThreads / kWave;
+constexpr int kNontemporal = 2;    // cache-policy bits of a buffer load: streaming
 
 // Radix-3 unpack of one word (20 weights): d[t] holds the offset codes of
 // k = 20j + 4t + b in byte b.
@@ -150,15 +152,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
       WRITE_ACC ? static_cast<int>(static_cast<int64_t>(M) * N * 4) : 0, 0x00020000);
   const uint32_t units32 = static_cast<uint32_t>(units);
   const uint32_t N32 = static_cast<uint32_t>(N);
+  // A group's 16 rows are one block of the interleaved row order: load
+  // instruction cs reads chunk cs of the block, one contiguous KiB when the
+  // block and the chunk are full (unit_offset in closed form).  The loads are
+  // nontemporal: every byte is used once.
   auto load_batch = [&](int b, bool valid, uint4 (&r)[kUnroll]) {
     const int gi = b / bpg;
     const int cb = b - gi * bpg;
-    const uint32_t row_off = static_cast<uint32_t>(n_base + gi * kRowsPerWave + j) * units32 * 16u;
+    const uint32_t n0 = static_cast<uint32_t>(n_base + gi * kRowsPerWave);
+    const uint32_t R = N32 > n0 ? min(16u, N32 - n0) : 0u;  // rows of the block
+    const uint32_t blk = n0 * units32 * 16u;
+    const bool row_ok = valid && static_cast<uint32_t>(j) < R;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t un = static_cast<uint32_t>(cb * kUnroll + u) * 4u + g;
-      const uint32_t off = (valid && un < units32) ? row_off + 16u * un : kOff;
-      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off, 0, 0);
+      const uint32_t cs = static_cast<uint32_t>(cb * kUnroll + u);
+      const uint32_t un = cs * 4u + g;
+      const uint32_t W = min(4u, units32 - min(units32, 4u * cs));  // units of chunk cs
+      const uint32_t off = (row_ok && un < units32) ? blk + (cs * R * 4u + j * W + g) * 16u : kOff;
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off, 0, kNontemporal);
       r[u] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };

@@ -104,9 +104,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
   const int a_r = tid >> 3, a_c = tid & 7;
   const int b_r = tid >> 1, b_c = tid & 1;
   const uint32_t voff_a = static_cast<uint32_t>(m0 + a_r) * kp32 + 16u * a_c;
-  const uint32_t voff_b = static_cast<uint32_t>(n0 + b_r) * (kp32 >> 2) + 16u * b_c;
   const uint32_t a_row_step = (THREADS / 8) * kp32;          // rows of activation codes per q
-  const uint32_t b_row_step = (THREADS / 2) * (kp32 >> 2);   // rows of packed words per q
+  // packed row b_n in the interleaved row order (see unit_offset): block base,
+  // row within the block, rows of the block
+  static_assert(B_LOADS == 1, "one packed slot per thread per stage");
+  const uint32_t units = kp32 >> 6;
+  const uint32_t N32 = static_cast<uint32_t>(N);
+  const uint32_t b_n = static_cast<uint32_t>(n0 + b_r);
+  const bool b_ok = b_n < N32;
+  const uint32_t b_blk = (b_n & ~15u) * units * 16u;
+  const uint32_t b_j = b_n & 15u;
+  const uint32_t b_R = b_ok ? min(16u, N32 - (b_n & ~15u)) : 0u;
   // LDS destinations (swizzled)
   int a_dst[A_LOADS], b_dst[B_LOADS];  // b_dst: LDS offset of the slot's first 8-byte half
 #pragma unroll
@@ -125,14 +133,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
     constexpr int S = decltype(set_tag)::value;
     const uint32_t k0 = static_cast<uint32_t>(it) * BK;
     const uint32_t a_adj = (k0 + 16u * a_c >= kp32) ? 64u : 0u;
-    const uint32_t b_adj = (k0 + 64u * b_c >= kp32) ? 16u : 0u;
+    // unit 2 it + b_c of the row; past Kp (final half stage) the unit before it
+    uint32_t u = 2u * static_cast<uint32_t>(it) + static_cast<uint32_t>(b_c);
+    u = u >= units ? u - 1u : u;
+    const uint32_t cu = u >> 2;
+    const uint32_t W = min(4u, units - 4u * cu);
+    const uint32_t voff_b = b_ok ? b_blk + (cu * b_R * 4u + b_j * W + (u & 3u)) * 16u : 0x80000000u;
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q)
       ra[S][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a + k0 - a_adj, q * a_row_step, 0);
-#pragma unroll
-    for (int q = 0; q < B_LOADS; ++q)
-      if (B_ALL || tid < B_SLOTS)
-        rb[S][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b + (k0 >> 2) - b_adj, q * b_row_step, 0);
+    if (B_ALL || tid < B_SLOTS)
+      rb[S][0] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, 0, 0);
   };
   auto swrite = [&](char* st, auto set_tag) {
     constexpr int S = decltype(set_tag)::value;

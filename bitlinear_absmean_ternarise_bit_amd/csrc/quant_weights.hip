@@ -202,7 +202,8 @@ __device__ __forceinline__ uint32_t offset_code(float w, float d, bool valid) {
 
 // Ternarise and pack.  Each lane turns four consecutive weights (k = 4f..4f+3)
 // into the four bytes' bit pair 2i of word f/4 (i = f%4); four adjacent lanes
-// OR their parts into one word.
+// OR their parts into one word, stored at its place in the interleaved row
+// order (unit_offset).
 template <bool VEC>
 __global__ __launch_bounds__(256) void ternarise_pack_kernel(const float* __restrict__ W, int64_t N,
                                                              int64_t K, int64_t Kp,
@@ -231,7 +232,12 @@ __global__ __launch_bounds__(256) void ternarise_pack_kernel(const float* __rest
     part <<= 2 * i;
     part |= __shfl_xor(part, 1, 4);
     part |= __shfl_xor(part, 2, 4);
-    if (i == 0) packed[f >> 2] = part;
+    if (i == 0) {
+      const uint32_t wi = static_cast<uint32_t>(kq >> 4);  // word of the row
+      const uint32_t off = unit_offset(static_cast<uint32_t>(n), wi >> 2, static_cast<uint32_t>(N),
+                                       static_cast<uint32_t>(Kp >> 6));
+      packed[(off >> 2) + (wi & 3u)] = part;
+    }
   }
 }
 
@@ -269,7 +275,10 @@ __global__ __launch_bounds__(256) void ternarise_pack_r3_kernel(const float* __r
     uint32_t word = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) word |= ((256u * v[b] + 242u) / 243u) << (8 * b);
-    packed[f] = word;
+    const uint32_t wi = static_cast<uint32_t>(f - n * words_per_row);  // word of the row
+    const uint32_t off = unit_offset(static_cast<uint32_t>(n), wi >> 2, static_cast<uint32_t>(N),
+                                     static_cast<uint32_t>(words_per_row >> 2));
+    packed[(off >> 2) + (wi & 3u)] = word;
   }
 }
 

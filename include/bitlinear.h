@@ -29,12 +29,23 @@
  * -------------------------------------------------------------------------
  * Each weight is stored as a 2-bit code c = q + 1 in {0,1,2} (3 never occurs),
  * [PMV s3].  A row of K weights is padded to Kp = bitlinear_padded_k(K) (a
- * multiple of 64) with c = 1, i.e. zero weights, and stored as Kp/16
+ * multiple of 64) with c = 1, i.e. zero weights, and encoded as Kp/16
  * little-endian uint32 words; bits [8b+2i, 8b+2i+1] of word j hold the code of
  * k = 16j + 4i + b.  So `(word >> 2i) & 0x03030303` is four int8 codes for
- * k = 16j+4i .. 16j+4i+3.  Rows follow each other with no gap:
- * packed is uint32[N][Kp/16], bitlinear_packed_bytes(N, K) bytes.  The buffer
- * carries no header: a forward must be given the K it was packed with.
+ * k = 16j+4i .. 16j+4i+3.
+ *
+ * Memory order (both formats): a row is a run of U 16-byte units (here four
+ * words, U = Kp/64).  Rows are stored in blocks of 16 consecutive rows (the
+ * last block holds N % 16 rows if that is not 0) and each block's units in
+ * chunks of 4 consecutive units (the last chunk holds U % 4 units if that is
+ * not 0); within a chunk, each row of the block in turn stores its units of
+ * that chunk contiguously.  Unit u of row n is therefore at byte
+ *     16*b*U*16 + c*R*64 + j*W*16 + (u%4)*16,
+ * with b = n/16, j = n%16, c = u/4, R = min(16, N - 16b), W = min(4, U - 4c).
+ * A full chunk (16 rows x 4 units) is one contiguous KiB, which the decode
+ * kernel reads with one load instruction; a single row (N = 1) is stored
+ * row-major.  The whole buffer is bitlinear_packed_bytes(N, K) = N*Kp/4 bytes
+ * and carries no header: a forward must be given the N and K it was packed with.
  */
 #ifndef BITLINEAR_H
 #define BITLINEAR_H
@@ -202,10 +213,11 @@ int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, 
  *
  * Format (this library's own; the article fixes only the count): a row of K
  * weights is padded with c = 1 to Kp3 = bitlinear_r3_padded_k(K), a multiple
- * of 80, and stored as Kp3/5 bytes; rows follow each other with no gap.  Byte
- * 4j + b of a row (b = 0..3) holds the five weights k = 20j + 4t + b,
- * t = 0..4, as ceil(256 * v / 243) with v = sum_t c_t * 3^(4 - t).  13 byte
- * values never occur.  The buffer carries no header.
+ * of 80, and encoded as Kp3/5 bytes.  Byte 4j + b of a row (b = 0..3) holds
+ * the five weights k = 20j + 4t + b, t = 0..4, as ceil(256 * v / 243) with
+ * v = sum_t c_t * 3^(4 - t); 13 byte values never occur.  Rows are stored in
+ * the interleaved memory order described at the top of this file, with
+ * 16-byte units of 80 weights (U = Kp3/80).  The buffer carries no header.
  */
 
 /* Kp3: K rounded up to a multiple of 80. */
