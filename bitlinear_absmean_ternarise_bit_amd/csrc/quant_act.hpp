@@ -47,6 +47,34 @@ __device__ __forceinline__ float load_one(const void* row, int64_t k) {
   else return bf16_to_f32(static_cast<const uint16_t*>(row)[k]);
 }
 
+// Codes of one 16-byte chunk (P values) with scale s, stored at dst; returns
+// their sum.
+template <int DT>
+__device__ __forceinline__ int quantize_chunk(const uint4 v, float s, int8_t* __restrict__ dst) {
+  constexpr int P = ActTraits<DT>::kPerChunk;
+  float f[P];
+  chunk_to_f32<DT>(v, f);
+  int sum = 0;
+  uint32_t w[P / 4];
+#pragma unroll
+  for (int q = 0; q < P / 4; ++q) {
+    uint32_t packedq = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int code = act_code(f[4 * q + b], s);
+      sum += code;
+      packedq |= (static_cast<uint32_t>(code) & 0xffu) << (8 * b);
+    }
+    w[q] = packedq;
+  }
+  if constexpr (P == 8) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else {
+    *reinterpret_cast<uint32_t*>(dst) = w[0];
+  }
+  return sum;
+}
+
 // Quantise row `row` (K values) into dst[0..Kp) (zeros in [K, Kp)); every lane
 // of the wave must call it.  Returns gamma_A and the code sum in all lanes.
 template <int DT, bool VEC>
@@ -54,6 +82,42 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, 
                                                   int lane, int8_t* __restrict__ dst,
                                                   float& gamma_a, int& codesum) {
   constexpr int P = ActTraits<DT>::kPerChunk;
+  if constexpr (VEC) {
+    // a row of at most four chunks per lane stays in registers between the
+    // two passes: one read of X instead of two
+    const uint4* r4 = static_cast<const uint4*>(row);
+    const int64_t nc = K / P;
+    if (nc <= 4 * kWave) {
+      uint4 v[4];
+      float mx = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = lane + u * kWave;
+        v[u] = r4[c < nc ? c : nc - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float f[P];
+        chunk_to_f32<DT>(v[u], f);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < P; ++i) m = fmaxf(m, fabsf(f[i]));
+        mx = (lane + u * kWave < nc) ? fmaxf(mx, m) : mx;
+      }
+      mx = wave_max(mx);
+      const float s = __fdiv_rn(127.0f, __fadd_rn(mx, kEps));
+      int sum = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = lane + u * kWave;
+        if (c < nc) sum += quantize_chunk<DT>(v[u], s, dst + c * P);
+      }
+      for (int64_t k = K + lane; k < Kp; k += kWave) dst[k] = 0;
+      gamma_a = mx;
+      codesum = wave_sum(sum);
+      return;
+    }
+  }
   float mx = 0.0f;
   if constexpr (VEC) {
     // four 16-byte loads in flight per lane; chunks past the row re-read the
@@ -87,27 +151,7 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, 
   if constexpr (VEC) {
     const uint4* r4 = static_cast<const uint4*>(row);
     const int64_t nc = K / P;
-    for (int64_t c = lane; c < nc; c += kWave) {
-      float f[P];
-      chunk_to_f32<DT>(r4[c], f);
-      uint32_t w[P / 4];
-#pragma unroll
-      for (int q = 0; q < P / 4; ++q) {
-        uint32_t packedq = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int code = act_code(f[4 * q + b], s);
-          sum += code;
-          packedq |= (static_cast<uint32_t>(code) & 0xffu) << (8 * b);
-        }
-        w[q] = packedq;
-      }
-      if constexpr (P == 8) {
-        *reinterpret_cast<uint2*>(dst + c * P) = make_uint2(w[0], w[1]);
-      } else {
-        *reinterpret_cast<uint32_t*>(dst + c * P) = w[0];
-      }
-    }
+    for (int64_t c = lane; c < nc; c += kWave) sum += quantize_chunk<DT>(r4[c], s, dst + c * P);
   } else {
     for (int64_t k = lane; k < K; k += kWave) {
       const int code = act_code(load_one<DT>(row, k), s);
