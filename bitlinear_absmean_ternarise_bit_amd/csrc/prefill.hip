@@ -53,7 +53,8 @@ template <int BM, int BN, int WM, int WN, bool WRITE_ACC>
 __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ gamma_a,
     const int32_t* __restrict__ rowsum, int64_t M, int64_t Kp, const uint32_t* __restrict__ packed,
-    int64_t N, const float* __restrict__ gamma, float* __restrict__ Y, int32_t* __restrict__ acc,
+    int64_t N, int64_t ldy, const float* __restrict__ gamma, float* __restrict__ Y,
+    int32_t* __restrict__ acc,
     int tiles_m, int tiles_n, int bytes_a, int bytes_b) {
   constexpr int A_BYTES = BM * 128;
   constexpr int B_BYTES = BN * 32;
@@ -264,18 +265,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
         const int64_t n = n0 + wn * (BN / WN) + ni * 32 + lr;
         if (n < N) {
           const int v = c[mi][ni][r] - rs;
-          if constexpr (WRITE_ACC) acc[m * N + n] = v;
-          Y[m * N + n] = __fmul_rn(static_cast<float>(v), scale);
+          if constexpr (WRITE_ACC) acc[m * ldy + n] = v;
+          Y[m * ldy + n] = __fmul_rn(static_cast<float>(v), scale);
         }
       }
     }
   }
 }
 
+// Rows [0, N) of the packed matrix against the tokens; Y and acc have row
+// stride ldy (N when the launch covers all output columns).
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_tile(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum, int64_t M,
-                       int64_t Kp, const uint32_t* packed, int64_t N, const float* gamma, float* Y,
-                       int32_t* acc, hipStream_t stream) {
+                       int64_t Kp, const uint32_t* packed, int64_t N, int64_t ldy, const float* gamma,
+                       float* Y, int32_t* acc, hipStream_t stream) {
   // Buffer offsets are 32-bit: run the tokens in chunks of < 2^31 code bytes.
   const int64_t chunk = ((int64_t(1) << 31) - 1) / Kp / BM * BM;
   const int bytes_b = static_cast<int>(N * (Kp / 4));
@@ -287,17 +290,19 @@ hipError_t launch_tile(const int8_t* Xq, const float* gamma_a, const int32_t* ro
     const int bytes_a = static_cast<int>(Mc * Kp);
     if (acc)
       prefill_gemm_kernel<BM, BN, WM, WN, true><<<blocks, 64 * WM * WN, 0, stream>>>(
-          Xq + r0 * Kp, gamma_a + r0, rowsum + r0, Mc, Kp, packed, N, gamma, Y + r0 * N, acc + r0 * N,
-          tiles_m, tiles_n, bytes_a, bytes_b);
+          Xq + r0 * Kp, gamma_a + r0, rowsum + r0, Mc, Kp, packed, N, ldy, gamma, Y + r0 * ldy,
+          acc + r0 * ldy, tiles_m, tiles_n, bytes_a, bytes_b);
     else
       prefill_gemm_kernel<BM, BN, WM, WN, false><<<blocks, 64 * WM * WN, 0, stream>>>(
-          Xq + r0 * Kp, gamma_a + r0, rowsum + r0, Mc, Kp, packed, N, gamma, Y + r0 * N, nullptr,
-          tiles_m, tiles_n, bytes_a, bytes_b);
+          Xq + r0 * Kp, gamma_a + r0, rowsum + r0, Mc, Kp, packed, N, ldy, gamma, Y + r0 * ldy,
+          nullptr, tiles_m, tiles_n, bytes_a, bytes_b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
+
+constexpr int64_t kCUs = 256;  // compute units of an MI355X: one workgroup each
 
 }  // namespace
 
@@ -307,13 +312,32 @@ hipError_t launch_prefill_gemm(const int8_t* Xq, const float* gamma_a, const int
   const int64_t Kp = padded_k(K);
   // One workgroup per CU.  The 256 x 256 tile (8 waves of 64 x 128) has the
   // best ratio of matrix-core work to LDS traffic; smaller tiles are used only
-  // when the big one would leave more than a quarter of the 256 CUs idle.
+  // when the big one would leave more than a quarter of the CUs idle.
   auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  if (tiles(256, 256) >= 192)
-    return launch_tile<256, 256, 4, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
+  const int64_t big = tiles(256, 256);
+  const int64_t rounds = big / kCUs;
+  const int64_t rest = big - rounds * kCUs;
+  // A few rounds of big tiles with a short last round: the first output
+  // columns take whole rounds of big tiles and the rest one round of
+  // 128 x 256 tiles (two launches; the packed rows of the second start at a
+  // multiple of 16, so they are a contiguous part of the buffer).
+  if (rounds >= 1 && rounds < 4 && rest > 0 && rest * 4 < 3 * kCUs) {
+    const int64_t tm_big = (M + 255) / 256, tm_half = (M + 127) / 128;
+    int64_t nA = (rounds * kCUs / tm_big) * 256;
+    while (nA > 0 && tm_half * ((N - nA + 255) / 256) > kCUs) nA -= 256;
+    if (nA > 0 && nA < N) {
+      hipError_t e = launch_tile<256, 256, 4, 2>(Xq, gamma_a, rowsum, M, Kp, packed, nA, N, gamma, Y,
+                                                 acc, stream);
+      if (e != hipSuccess) return e;
+      return launch_tile<128, 256, 2, 4>(Xq, gamma_a, rowsum, M, Kp, packed + nA * (Kp / 16), N - nA, N,
+                                         gamma, Y + nA, acc ? acc + nA : nullptr, stream);
+    }
+  }
+  if (big >= 192)
+    return launch_tile<256, 256, 4, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, N, gamma, Y, acc, stream);
   if (tiles(128, 256) >= 192)
-    return launch_tile<128, 256, 2, 4>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
-  return launch_tile<128, 128, 2, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, gamma, Y, acc, stream);
+    return launch_tile<128, 256, 2, 4>(Xq, gamma_a, rowsum, M, Kp, packed, N, N, gamma, Y, acc, stream);
+  return launch_tile<128, 128, 2, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, N, gamma, Y, acc, stream);
 }
 
 }  // namespace bitlinear

@@ -160,6 +160,8 @@ FORWARD_CASES = [
     (40, 4096, 1000, "bf16", "auto"),
     (1024, 640, 6144, "bf16", "prefill"),   # 128 x 256 tiles
     (2000, 1050, 6200, "f32", "prefill"),   # 256 x 256 tiles, ragged M, N and a half K stage
+    (2048, 200, 11008, "bf16", "prefill"),  # 1.34 rounds of big tiles: columns split over two launches
+    (2048, 200, 11000, "f32", "prefill"),   # same split, ragged N: partial last row block in the second
 ]
 
 
