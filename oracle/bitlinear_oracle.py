@@ -21,7 +21,13 @@ quantisation, the BitLinear layer and Zero-GEMM).  Its sections:
   example, and the single rescale of A_q x W_q^T by gamma_A * gamma / 127;
 * [PMV §3]  the memory wall: 2-bit packing, 0.25 byte per weight;
 * [PMV §4]  how bitnet.cpp speeds up CPU inference: the 81-entry LUT figure
-  for four weights and the Radix-3 packing of five weights per byte.
+  for four weights and the Radix-3 packing of five weights per byte;
+* [PMV §5]  the trade-offs section: attention, SwiGLU-style activations and
+  RMSNorm stay in floating point (or INT8).
+
+[MBC] is the shadowgraph.io page on a hybrid multimodal architecture around
+bitnet.cpp; its bit_layers.py section lists BitLinear, the ternary and 8-bit
+quantisers and ReLU^2 as the activation BitNet specifies.
 
 Readings where the article leaves a step open:
 
@@ -440,3 +446,58 @@ def sampled_forward(X: np.ndarray, q: np.ndarray, gamma, rows, cols) -> Dict[str
     acc = zero_gemm(Xq, np.asarray(q)[cols])
     return {"gamma_a": gA, "Xq": Xq, "rowsum": rowsum, "acc": acc,
             "Y": dequant(acc, gamma, gA)}
+
+
+# ---------------------------------------------------------------------------
+# BitNet FFN block: BitLinear up -> ReLU^2 -> BitLinear down
+# [MBC bit_layers.py: ReLU^2 activation; PMV §5: non-linear parts in floating
+# point; PMV §1 AbsMax: each BitLinear quantises its own input per token]
+#
+# Reading: the block is Y = BitLinear_down(ReLU^2(BitLinear_up(X))) with no
+# norm inside (norms stay outside, in floating point).  The up projection's
+# output H is formed in float32 as the kernels form every output:
+# H = fp32(fp32(acc) * s), s = fp32(fp32(gamma * gamma_A) / 127).  Because H
+# decides the INT8 codes of the down projection, both sides form it in that
+# same precision; A = ReLU^2(H) = fp32(max(H, 0)^2).  The final Y is rescaled
+# like any BitLinear output (float64, rounded once).
+# ---------------------------------------------------------------------------
+
+def dequant_f32(acc: np.ndarray, gamma, gamma_a: np.ndarray) -> np.ndarray:
+    """H[m, n] = fp32(fp32(acc) * fp32(fp32(gamma * gamma_A[m]) / 127)): three float32 roundings."""
+    acc = np.asarray(acc)
+    g = np.float32(gamma)
+    ga = np.asarray(gamma_a, dtype=np.float32)
+    s = ((g * ga).astype(np.float32) / np.float32(127.0)).astype(np.float32)
+    h = acc.astype(np.float32) * s[:, None]
+    assert h.dtype == np.float32
+    return h
+
+
+def relu2(H: np.ndarray) -> np.ndarray:
+    """ReLU^2 in float32: fp32(max(h, 0) * max(h, 0))  [MBC bit_layers.py]."""
+    r = np.maximum(np.asarray(H, dtype=np.float32), np.float32(0.0))
+    a = r * r
+    assert a.dtype == np.float32
+    return a + np.float32(0.0)  # -0.0 -> +0.0
+
+
+def ffn_from_codes(X, q_up, g_up, q_down, g_down) -> Dict[str, np.ndarray]:
+    """The FFN block from ternary codes and scales of both projections."""
+    gA, Xq, rowsum = absmax_quantize(X)
+    acc1 = zero_gemm(Xq, q_up)
+    H = dequant_f32(acc1, g_up, gA)
+    A = relu2(H)
+    gA2, Aq, rowsum2 = absmax_quantize(A)
+    acc2 = zero_gemm(Aq, q_down)
+    Y = dequant(acc2, g_down, gA2)
+    return {"gamma_a": gA, "Xq": Xq, "acc1": acc1, "H": H, "A": A, "gamma_a2": gA2, "Aq": Aq,
+            "rowsum2": rowsum2, "acc2": acc2, "Y": Y}
+
+
+def ffn_forward(X: np.ndarray, W_up: np.ndarray, W_down: np.ndarray) -> Dict[str, np.ndarray]:
+    """Y = BitLinear_down(ReLU^2(BitLinear_up(X))); W_up [F, D], W_down [D_out, F]."""
+    g_up, q_up, _ = quantize_weights(W_up)
+    g_dn, q_dn, _ = quantize_weights(W_down)
+    out = ffn_from_codes(X, q_up, g_up, q_dn, g_dn)
+    out.update({"gamma_up": g_up, "q_up": q_up, "gamma_down": g_dn, "q_down": q_dn})
+    return out
