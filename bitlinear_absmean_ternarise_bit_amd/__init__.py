@@ -25,6 +25,7 @@ __all__ = [
     "forward_quantized",
     "max_decode_m",
     "decode_fits",
+    "ffn_forward",
     "r3_padded_k",
     "r3_row_bytes",
     "r3_decode_fits",
@@ -310,3 +311,46 @@ def forward_r3(X, packed, gamma, K: int | None = None, return_acc: bool = False,
               lib.bitlinear_forward_r3(L, _ptr(X), _x_dtype(X), M, K, _ptr(packed), N, _ptr(gamma),
                                        _ptr(Y), _ptr(acc), _stream(X)))
     return (Y, acc) if return_acc else Y
+
+
+# ---- the BitNet FFN block --------------------------------------------------
+
+def ffn_forward(X, up, down, path: str = "auto", return_hidden: bool = False, out=None, workspace=None):
+    """Y = BitLinear_down(ReLU^2(BitLinear_up(X))).
+
+    ``up`` = (packed [F, words(D)], gamma [1]) and ``down`` = (packed [D_out, words(F)],
+    gamma [1]) as :func:`quantize_weights` returns them, with X [M, D]; or X
+    [L, M, D] with packed [L, ...] and gamma [L] for L layers.  Returns Y float32
+    [(L,) M, D_out] (and the hidden ReLU^2 activations [(L,) M, F] if asked).
+    """
+    torch = _torch()
+    (pu, gu), (pd, gd) = up, down
+    for t, nm in ((X, "X"), (pu, "packed_up"), (gu, "gamma_up"), (pd, "packed_down"), (gd, "gamma_down")):
+        _require_cuda(t, nm)
+    batched = X.dim() == 3
+    if batched:
+        L, M, D = X.shape
+        F, Do = pu.shape[1], pd.shape[1]
+        if pu.dim() != 3 or pd.dim() != 3 or pu.shape[0] != L or pd.shape[0] != L or gu.numel() != L \
+                or gd.numel() != L:
+            raise ValueError("inconsistent batched shapes")
+    else:
+        L = 1
+        M, D = X.shape
+        F, Do = pu.shape[0], pd.shape[0]
+    if pu.shape[-1] != packed_words(D) or pd.shape[-1] != packed_words(F):
+        raise ValueError("packed weights do not match D and F")
+    lib = abi.load()
+    shape = (L, M, Do) if batched else (M, Do)
+    Y = out if out is not None else torch.empty(shape, dtype=torch.float32, device=X.device)
+    hid = torch.empty((L, M, F) if batched else (M, F), dtype=torch.float32, device=X.device) \
+        if return_hidden else None
+    if workspace is None:
+        ws_bytes = lib.bitlinear_ffn_workspace_bytes(L, M, D, F)
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=X.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    abi.check("bitlinear_ffn_forward",
+              lib.bitlinear_ffn_forward(L, _ptr(X), _x_dtype(X), M, D, F, Do, _ptr(pu), _ptr(gu), _ptr(pd),
+                                        _ptr(gd), _ptr(Y), _ptr(hid), _PATHS[path], _ptr(workspace), ws_bytes,
+                                        _stream(X)))
+    return (Y, hid) if return_hidden else Y

@@ -173,6 +173,76 @@ int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, 
                                   static_cast<hipStream_t>(stream)));
 }
 
+size_t bitlinear_ffn_workspace_bytes(int64_t L, int64_t M, int64_t D, int64_t F) {
+  if (L < 1 || M < 1 || D < 1 || F < 1) return 0;
+  const size_t hidden = align256(static_cast<size_t>(L) * static_cast<size_t>(M) * static_cast<size_t>(F) * 4);
+  const size_t codes = prefill_ws_bytes(M, D) > prefill_ws_bytes(M, F) ? prefill_ws_bytes(M, D)
+                                                                       : prefill_ws_bytes(M, F);
+  return hidden + codes;
+}
+
+int bitlinear_ffn_forward(int64_t L, const void* X, int x_dtype, int64_t M, int64_t D, int64_t F,
+                          int64_t D_out, const uint32_t* packed_up, const float* gamma_up,
+                          const uint32_t* packed_down, const float* gamma_down, float* Y,
+                          float* hidden, int path, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!X || !packed_up || !gamma_up || !packed_down || !gamma_down || !Y) return BITLINEAR_ERR_NULL;
+  if (L < 1 || L > (int64_t(1) << 20)) return BITLINEAR_ERR_SHAPE;
+  int st = check_mnk(M, F, D);
+  if (st) return st;
+  st = check_mnk(M, D_out, F);
+  if (st) return st;
+  if (static_cast<uint64_t>(L) * static_cast<uint64_t>(M) * static_cast<uint64_t>(F > D_out ? F : D_out) >=
+      (uint64_t(1) << 40))
+    return BITLINEAR_ERR_SHAPE;
+  st = check_x(X, x_dtype);
+  if (st) return st;
+  if (path != BITLINEAR_PATH_AUTO && path != BITLINEAR_PATH_DECODE && path != BITLINEAR_PATH_PREFILL)
+    return BITLINEAR_ERR_ARG;
+  if (!aligned(packed_up, 16) || !aligned(packed_down, 16) || !aligned(gamma_up, 4) ||
+      !aligned(gamma_down, 4) || !aligned(Y, 4) || (hidden && !aligned(hidden, 16)))
+    return BITLINEAR_ERR_ALIGN;
+  const bool fits = decode_fits(M, D, F) && decode_fits(M, F, D_out) &&
+                    L * ((F > D_out ? F : D_out) + 63) / 64 < (int64_t(1) << 31);
+  if (path == BITLINEAR_PATH_DECODE && !fits) return BITLINEAR_ERR_SHAPE;
+  const bool decode = path == BITLINEAR_PATH_DECODE || (path == BITLINEAR_PATH_AUTO && fits);
+  const size_t hidden_bytes = align256(static_cast<size_t>(L) * static_cast<size_t>(M) * static_cast<size_t>(F) * 4);
+  const size_t codes_bytes = decode ? 0
+                                    : (prefill_ws_bytes(M, D) > prefill_ws_bytes(M, F) ? prefill_ws_bytes(M, D)
+                                                                                       : prefill_ws_bytes(M, F));
+  const size_t need = (hidden ? 0 : hidden_bytes) + codes_bytes;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return BITLINEAR_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return BITLINEAR_ERR_ALIGN;
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* A = hidden ? hidden : reinterpret_cast<float*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t up_words = F * (padded_k(D) / 16), down_words = D_out * (padded_k(F) / 16);
+  if (decode) {
+    // all layers' hidden activations in one launch, then all down projections
+    hipError_t e = launch_decode(X, x_dtype, M, D, packed_up, F, gamma_up, A, nullptr, L, s, true);
+    if (e != hipSuccess) return BITLINEAR_ERR_HIP;
+    return hip_status(launch_decode(A, BITLINEAR_F32, M, F, packed_down, D_out, gamma_down, Y, nullptr, L, s));
+  }
+  PrefillWs w = prefill_ws(ws + (hidden ? 0 : hidden_bytes), M, D > F ? D : F);
+  const int esize = x_dtype == BITLINEAR_F32 ? 4 : 2;
+  for (int64_t l = 0; l < L; ++l) {
+    const char* Xl = static_cast<const char*>(X) + l * M * D * esize;
+    float* Al = A + l * M * F;
+    hipError_t e = launch_act_quant(Xl, x_dtype, M, D, w.xq, w.ga, w.rs, s);
+    if (e == hipSuccess)
+      e = launch_prefill_gemm(w.xq, w.ga, w.rs, M, D, packed_up + l * up_words, F, gamma_up + l, Al, nullptr, s,
+                              true);
+    if (e == hipSuccess) e = launch_act_quant(Al, BITLINEAR_F32, M, F, w.xq, w.ga, w.rs, s);
+    if (e == hipSuccess)
+      e = launch_prefill_gemm(w.xq, w.ga, w.rs, M, F, packed_down + l * down_words, D_out, gamma_down + l,
+                              Y + l * M * D_out, nullptr, s);
+    if (e != hipSuccess) return BITLINEAR_ERR_HIP;
+  }
+  return BITLINEAR_OK;
+}
+
 int64_t bitlinear_r3_padded_k(int64_t K) { return K < 1 ? 0 : r3_padded_k(K); }
 
 size_t bitlinear_r3_packed_bytes(int64_t N, int64_t K) {

@@ -104,7 +104,11 @@ __device__ __forceinline__ void unit_operands(const uint4& r, v4i (&bop)[Format<
 // consecutive units of 16 rows); the loads of batch b+1 are issued before
 // batch b is contracted, and the first batch is in flight while phase A
 // quantises X.  Kp is the LDS row length in codes (units * kPerUnit).
-template <int FMT, int DT, bool VEC, bool WRITE_ACC>
+// Epilogues: Y only, Y and the INT32 accumulators, or ReLU^2 of Y (the hidden
+// activation of a BitNet FFN block).
+enum Epilogue { kEpiY = 0, kEpiAcc = 1, kEpiRelu2 = 2 };
+
+template <int FMT, int DT, bool VEC, int EPI>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const void* __restrict__ X, int M, int64_t K, int64_t Kp, int64_t units,
     const uint32_t* __restrict__ packed, int64_t N, const float* __restrict__ gamma,
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   X = static_cast<const char*>(X) + layer * M * K * esize;
   packed += layer * N * units * 4;
   Y += layer * M * N;
-  if constexpr (WRITE_ACC) acc += layer * M * N;
+  if constexpr (EPI == kEpiAcc) acc += layer * M * N;
   gamma += layer;
 
   const int wave = threadIdx.x >> 6;
@@ -148,8 +152,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const __amdgpu_buffer_rsrc_t ysrc = __builtin_amdgcn_make_buffer_rsrc(
       Y, 0, static_cast<int>(static_cast<int64_t>(M) * N * 4), 0x00020000);
   const __amdgpu_buffer_rsrc_t asrc = __builtin_amdgcn_make_buffer_rsrc(
-      WRITE_ACC ? static_cast<void*>(acc) : static_cast<void*>(Y), 0,
-      WRITE_ACC ? static_cast<int>(static_cast<int64_t>(M) * N * 4) : 0, 0x00020000);
+      (EPI == kEpiAcc) ? static_cast<void*>(acc) : static_cast<void*>(Y), 0,
+      (EPI == kEpiAcc) ? static_cast<int>(static_cast<int64_t>(M) * N * 4) : 0, 0x00020000);
   const uint32_t units32 = static_cast<uint32_t>(units);
   const uint32_t N32 = static_cast<uint32_t>(N);
   // A group's 16 rows are one block of the interleaved row order: load
@@ -225,10 +229,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
       const int ic = i < M ? i : M - 1;
       const int v = c[r] - s_rs[ic];
       const float scale = __fdiv_rn(__fmul_rn(gm, s_ga[ic]), 127.0f);
-      const float y = __fmul_rn(static_cast<float>(v), scale);
+      float y = __fmul_rn(static_cast<float>(v), scale);
+      if constexpr (EPI == kEpiRelu2) {
+        const float r = fmaxf(y, 0.0f);
+        y = __fmul_rn(r, r) + 0.0f;  // + 0: no negative zero
+      }
       const uint32_t off = (last && i < M && n < N32) ? (static_cast<uint32_t>(i) * N32 + n) * 4u : kOff;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), ysrc, off, 0, 0);
-      if constexpr (WRITE_ACC) __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(v), asrc, off, 0, 0);
+      if constexpr (EPI == kEpiAcc) __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(v), asrc, off, 0, 0);
     }
     c = last ? zero : c;
   };
@@ -261,49 +269,58 @@ int pick_groups(int64_t L, int64_t N) {
 
 template <int FMT, int DT, bool VEC>
 hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed, int64_t N,
-                    const float* gamma, float* Y, int32_t* acc, int64_t L, hipStream_t stream) {
+                    const float* gamma, float* Y, int32_t* acc, int64_t L, bool relu2,
+                    hipStream_t stream) {
   const int64_t Kp = FMT == 2 ? padded_k(K) : r3_padded_k(K);
   const int64_t units = Kp / Format<FMT>::kPerUnit;
   const int groups = pick_groups(L, N);
   const int64_t rows = int64_t(kWaves) * kRowsPerWave * groups;
   const int bpl = static_cast<int>((N + rows - 1) / rows);
-  const int64_t blocks = L * bpl;
+  const unsigned blocks = static_cast<unsigned>(L * bpl);
   const size_t lds = static_cast<size_t>(M) * static_cast<size_t>(Kp + 16);
+  const int m = static_cast<int>(M);
+  if constexpr (FMT == 2) {
+    if (relu2) {
+      decode_kernel<FMT, DT, VEC, kEpiRelu2><<<blocks, kDecodeThreads, lds, stream>>>(
+          X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups);
+      return hipGetLastError();
+    }
+  }
   if (acc)
-    decode_kernel<FMT, DT, VEC, true><<<static_cast<unsigned>(blocks), kDecodeThreads, lds, stream>>>(
-        X, static_cast<int>(M), K, Kp, units, packed, N, gamma, Y, acc, bpl, groups);
+    decode_kernel<FMT, DT, VEC, kEpiAcc><<<blocks, kDecodeThreads, lds, stream>>>(
+        X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups);
   else
-    decode_kernel<FMT, DT, VEC, false><<<static_cast<unsigned>(blocks), kDecodeThreads, lds, stream>>>(
-        X, static_cast<int>(M), K, Kp, units, packed, N, gamma, Y, acc, bpl, groups);
+    decode_kernel<FMT, DT, VEC, kEpiY><<<blocks, kDecodeThreads, lds, stream>>>(
+        X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups);
   return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t launch_fmt(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
-                      int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
+                      int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L, bool relu2,
                       hipStream_t stream) {
   const int esize = x_dtype == 0 ? 4 : 2;
   const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ((K * esize) % 16 == 0);
   if (x_dtype == 0)
-    return vec ? launch_v<FMT, 0, true>(X, M, K, packed, N, gamma, Y, acc, L, stream)
-               : launch_v<FMT, 0, false>(X, M, K, packed, N, gamma, Y, acc, L, stream);
-  return vec ? launch_v<FMT, 1, true>(X, M, K, packed, N, gamma, Y, acc, L, stream)
-             : launch_v<FMT, 1, false>(X, M, K, packed, N, gamma, Y, acc, L, stream);
+    return vec ? launch_v<FMT, 0, true>(X, M, K, packed, N, gamma, Y, acc, L, relu2, stream)
+               : launch_v<FMT, 0, false>(X, M, K, packed, N, gamma, Y, acc, L, relu2, stream);
+  return vec ? launch_v<FMT, 1, true>(X, M, K, packed, N, gamma, Y, acc, L, relu2, stream)
+             : launch_v<FMT, 1, false>(X, M, K, packed, N, gamma, Y, acc, L, relu2, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
                          int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
-                         hipStream_t stream) {
-  return launch_fmt<2>(X, x_dtype, M, K, packed, N, gamma, Y, acc, L, stream);
+                         hipStream_t stream, bool relu2) {
+  return launch_fmt<2>(X, x_dtype, M, K, packed, N, gamma, Y, acc, L, relu2, stream);
 }
 
 hipError_t launch_decode_r3(const void* X, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
                             int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
                             hipStream_t stream) {
   return launch_fmt<3>(X, x_dtype, M, K, reinterpret_cast<const uint32_t*>(packed), N, gamma, Y,
-                       acc, L, stream);
+                       acc, L, false, stream);
 }
 
 }  // namespace bitlinear

@@ -28,10 +28,11 @@ hipError_t launch_quantize_weights_r3(const float* W, int64_t N, int64_t K, uint
 hipError_t launch_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, int8_t* Xq,
                             float* gamma_a, int32_t* rowsum, hipStream_t stream);
 
-// a3 + a4 + a6 fused (decode, M <= kDecodeMaxM), L layers of one shape
+// a3 + a4 + a6 fused (decode, M <= kDecodeMaxM), L layers of one shape;
+// relu2: Y receives ReLU^2 of the output (a BitNet FFN block's hidden layer)
 hipError_t launch_decode(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
                          int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
-                         hipStream_t stream);
+                         hipStream_t stream, bool relu2 = false);
 
 // a3 + a4 + a6 fused, radix-3 weights
 hipError_t launch_decode_r3(const void* X, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
@@ -41,6 +42,7 @@ hipError_t launch_decode_r3(const void* X, int x_dtype, int64_t M, int64_t K, co
 // a5 + a6 (prefill): codes from launch_act_quant
 hipError_t launch_prefill_gemm(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum,
                                int64_t M, int64_t K, const uint32_t* packed, int64_t N,
-                               const float* gamma, float* Y, int32_t* acc, hipStream_t stream);
+                               const float* gamma, float* Y, int32_t* acc, hipStream_t stream,
+                               bool relu2 = false);
 
 }  // namespace bitlinear

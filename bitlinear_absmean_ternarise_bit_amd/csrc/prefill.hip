@@ -49,7 +49,9 @@ constexpr int kBufferFlags = 0x00020000;
 // are outstanding (vector-memory and export counters left free).
 constexpr int lgkmcnt_imm(int n) { return 15 | (3 << 14) | (7 << 4) | ((n & 15) << 8); }
 
-template <int BM, int BN, int WM, int WN, bool WRITE_ACC>
+// EPI: 0 = Y, 1 = Y and the INT32 accumulators, 2 = ReLU^2 of Y (the hidden
+// activation of a BitNet FFN block)
+template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ gamma_a,
     const int32_t* __restrict__ rowsum, int64_t M, int64_t Kp, const uint32_t* __restrict__ packed,
@@ -265,8 +267,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
         const int64_t n = n0 + wn * (BN / WN) + ni * 32 + lr;
         if (n < N) {
           const int v = c[mi][ni][r] - rs;
-          if constexpr (WRITE_ACC) acc[m * ldy + n] = v;
-          Y[m * ldy + n] = __fmul_rn(static_cast<float>(v), scale);
+          if constexpr (EPI == 1) acc[m * ldy + n] = v;
+          float y = __fmul_rn(static_cast<float>(v), scale);
+          if constexpr (EPI == 2) {
+            const float r = fmaxf(y, 0.0f);
+            y = __fmul_rn(r, r) + 0.0f;  // + 0: no negative zero
+          }
+          Y[m * ldy + n] = y;
         }
       }
     }
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_tile(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum, int64_t M,
                        int64_t Kp, const uint32_t* packed, int64_t N, int64_t ldy, const float* gamma,
-                       float* Y, int32_t* acc, hipStream_t stream) {
+                       float* Y, int32_t* acc, bool relu2, hipStream_t stream) {
   // Buffer offsets are 32-bit: run the tokens in chunks of < 2^31 code bytes.
   const int64_t chunk = ((int64_t(1) << 31) - 1) / Kp / BM * BM;
   const int bytes_b = static_cast<int>(N * (Kp / 4));
@@ -288,12 +295,16 @@ hipError_t launch_tile(const int8_t* Xq, const float* gamma_a, const int32_t* ro
     const int tiles_n = static_cast<int>((N + BN - 1) / BN);
     const unsigned blocks = static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n);
     const int bytes_a = static_cast<int>(Mc * Kp);
-    if (acc)
-      prefill_gemm_kernel<BM, BN, WM, WN, true><<<blocks, 64 * WM * WN, 0, stream>>>(
+    if (relu2)
+      prefill_gemm_kernel<BM, BN, WM, WN, 2><<<blocks, 64 * WM * WN, 0, stream>>>(
+          Xq + r0 * Kp, gamma_a + r0, rowsum + r0, Mc, Kp, packed, N, ldy, gamma, Y + r0 * ldy,
+          nullptr, tiles_m, tiles_n, bytes_a, bytes_b);
+    else if (acc)
+      prefill_gemm_kernel<BM, BN, WM, WN, 1><<<blocks, 64 * WM * WN, 0, stream>>>(
           Xq + r0 * Kp, gamma_a + r0, rowsum + r0, Mc, Kp, packed, N, ldy, gamma, Y + r0 * ldy,
           acc + r0 * ldy, tiles_m, tiles_n, bytes_a, bytes_b);
     else
-      prefill_gemm_kernel<BM, BN, WM, WN, false><<<blocks, 64 * WM * WN, 0, stream>>>(
+      prefill_gemm_kernel<BM, BN, WM, WN, 0><<<blocks, 64 * WM * WN, 0, stream>>>(
           Xq + r0 * Kp, gamma_a + r0, rowsum + r0, Mc, Kp, packed, N, ldy, gamma, Y + r0 * ldy,
           nullptr, tiles_m, tiles_n, bytes_a, bytes_b);
     const hipError_t e = hipGetLastError();
@@ -308,8 +319,10 @@ constexpr int64_t kCUs = 256;  // compute units of an MI355X: one workgroup each
 
 hipError_t launch_prefill_gemm(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum,
                                int64_t M, int64_t K, const uint32_t* packed, int64_t N,
-                               const float* gamma, float* Y, int32_t* acc, hipStream_t stream) {
+                               const float* gamma, float* Y, int32_t* acc, hipStream_t stream,
+                               bool relu2) {
   const int64_t Kp = padded_k(K);
+  if (relu2) acc = nullptr;
   // One workgroup per CU.  The 256 x 256 tile (8 waves of 64 x 128) has the
   // best ratio of matrix-core work to LDS traffic; smaller tiles are used only
   // when the big one would leave more than a quarter of the CUs idle.
@@ -327,17 +340,17 @@ hipError_t launch_prefill_gemm(const int8_t* Xq, const float* gamma_a, const int
     while (nA > 0 && tm_half * ((N - nA + 255) / 256) > kCUs) nA -= 256;
     if (nA > 0 && nA < N) {
       hipError_t e = launch_tile<256, 256, 4, 2>(Xq, gamma_a, rowsum, M, Kp, packed, nA, N, gamma, Y,
-                                                 acc, stream);
+                                                 acc, relu2, stream);
       if (e != hipSuccess) return e;
       return launch_tile<128, 256, 2, 4>(Xq, gamma_a, rowsum, M, Kp, packed + nA * (Kp / 16), N - nA, N,
-                                         gamma, Y + nA, acc ? acc + nA : nullptr, stream);
+                                         gamma, Y + nA, acc ? acc + nA : nullptr, relu2, stream);
     }
   }
   if (big >= 192)
-    return launch_tile<256, 256, 4, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, N, gamma, Y, acc, stream);
+    return launch_tile<256, 256, 4, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, N, gamma, Y, acc, relu2, stream);
   if (tiles(128, 256) >= 192)
-    return launch_tile<128, 256, 2, 4>(Xq, gamma_a, rowsum, M, Kp, packed, N, N, gamma, Y, acc, stream);
-  return launch_tile<128, 128, 2, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, N, gamma, Y, acc, stream);
+    return launch_tile<128, 256, 2, 4>(Xq, gamma_a, rowsum, M, Kp, packed, N, N, gamma, Y, acc, relu2, stream);
+  return launch_tile<128, 128, 2, 2>(Xq, gamma_a, rowsum, M, Kp, packed, N, N, gamma, Y, acc, relu2, stream);
 }
 
 }  // namespace bitlinear

@@ -8,6 +8,9 @@ Recipe (one ``numpy.random.default_rng(seed)`` per workload, seed 0 unless
 stated; draw order: W, then X, then any row/channel/token selections):
 
 * W = float32(sigma * standard_normal(N, K)) drawn in float64, rounded once.
+* FFN blocks (BitLinear up -> ReLU^2 -> BitLinear down) reuse a projection
+  workload's X and W as X and W_up, and draw W_down [D, F] with the same sigma
+  from a second generator, ``default_rng(seed + 1)``.
 * X = float32 draws of shape (M, K); when the workload runs in bfloat16 the
   float32 values are rounded to bfloat16 with round-half-to-even.
 
@@ -28,6 +31,9 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "make_workload",
+    "FfnWorkload",
+    "FFN_WORKLOADS",
+    "make_ffn_workload",
     "random_problem",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
@@ -156,3 +162,43 @@ def random_problem(M: int, K: int, N: int, seed: int, x_dtype: str = "f32",
     W = _gauss_w(rng, N, K, sigma)
     X, bits = _finish_x(x_scale * rng.standard_normal((M, K)), x_dtype)
     return Workload(f"gauss_m{M}_k{K}_n{N}_s{seed}", M, K, N, W, X, x_dtype, bits)
+
+
+@dataclass
+class FfnWorkload:
+    name: str
+    M: int
+    D: int
+    F: int
+    D_out: int
+    X: np.ndarray  # float32 [M, D]
+    x_dtype: str
+    X_bf16_bits: Optional[np.ndarray]
+    W_up: np.ndarray  # float32 [F, D]
+    W_down: np.ndarray  # float32 [D_out, F]
+    notes: dict = field(default_factory=dict)
+
+
+def _ffn_from(proj: str, sigma: float, name: str, seed: int) -> FfnWorkload:
+    P = make_workload(proj, seed)
+    rng = np.random.default_rng(seed + 1)
+    W_down = _gauss_w(rng, P.K, P.N, sigma)
+    return FfnWorkload(name, P.M, P.K, P.N, P.K, P.X, P.x_dtype, P.X_bf16_bits, P.W, W_down, dict(P.notes))
+
+
+FFN_WORKLOADS = {
+    # the small-batch decode FFN: d_model 2048, hidden 5632, 8 tokens
+    "ffn_block_decode_m8_d2048_f5632": lambda seed=0: _ffn_from(
+        "decode_ffn_up_m8_k2048_n5632", 0.02, "ffn_block_decode_m8_d2048_f5632", seed),
+    # the 7B-like prefill FFN: d_model 4096, hidden 11008, 2048 tokens
+    "ffn_block_prefill_m2048_d4096_f11008": lambda seed=0: _ffn_from(
+        "prefill_ffn_m2048_k4096_n11008", 0.015, "ffn_block_prefill_m2048_d4096_f11008", seed),
+}
+
+
+def make_ffn_workload(name: str, seed: int = 0) -> FfnWorkload:
+    try:
+        fn = FFN_WORKLOADS[name]
+    except KeyError:
+        raise KeyError(f"unknown FFN workload {name!r}; known: {sorted(FFN_WORKLOADS)}") from None
+    return fn(seed)

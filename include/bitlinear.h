@@ -8,7 +8,8 @@
  * (add/subtract/skip, INT32 accumulation, rescale by gamma_A * gamma / 127),
  * [PMV s3] the section on the memory wall (2-bit packing, 0.25 byte/weight),
  * [PMV s4] the section on how bitnet.cpp speeds up inference on CPUs (the
- * LUT figure and the Radix-3 packing of five weights per byte).
+ * LUT figure and the Radix-3 packing of five weights per byte), [PMV s5] its
+ * section on trade-offs and engineering challenges.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -202,6 +203,42 @@ int bitlinear_forward_quantized(const int8_t* Xq, const float* gamma_a, const in
 int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, int64_t K,
                               const uint32_t* packed, int64_t N, const float* gamma,
                               float* Y, void* stream);
+
+/* ---- the BitNet FFN block: BitLinear up -> ReLU^2 -> BitLinear down ----- */
+/*
+ * For l = 0..L-1:
+ *   H_l = BitLinear_up(X_l)            (packed_up: [F, D] ternary, gamma_up[l])
+ *   A_l = ReLU^2(H_l) = max(H_l, 0)^2  [MBC: bit_layers.py gives ReLU^2 as BitNet's
+ *                                       activation]
+ *   Y_l = BitLinear_down(A_l)          (packed_down: [D_out, F], gamma_down[l]);
+ *         A_l is quantised per token with AbsMax like any BitLinear input [PMV s1]
+ * [MBC] is the shadowgraph.io page on a multimodal architecture around
+ * bitnet.cpp.  Norms stay outside, in floating point [PMV s5: the trade-offs
+ * section].  H is formed in float32 exactly as every output here
+ * (fp32(acc) * fp32(fp32(gamma * gamma_A) / 127)) and A = fp32(r * r), r = max(H, 0).
+ *
+ * The up projection's epilogue applies ReLU^2, so the hidden layer is written
+ * once as float32 and read once by the down projection, whose quantiser reads
+ * it as its input.  Decode path (both projections fit the decode kernel): two
+ * launches for all L layers.  Prefill path: per layer, quantise X, GEMM with
+ * the ReLU^2 epilogue, quantise A, GEMM.
+ *
+ * X: device [L, M, D] float32 or bfloat16.  packed_up: L matrices of F rows,
+ * bitlinear_packed_bytes(F, D) bytes each, back to back; packed_down: L
+ * matrices of D_out rows, bitlinear_packed_bytes(D_out, F) bytes each.
+ * gamma_up, gamma_down: device float32 [L].  Y: device float32 [L, M, D_out].
+ * hidden: NULL, or device float32 [L, M, F], 16-byte aligned, receiving A.
+ * path: BITLINEAR_PATH_AUTO / _DECODE / _PREFILL as for bitlinear_forward_ex.
+ * workspace: >= bitlinear_ffn_workspace_bytes(L, M, D, F), 256-byte aligned
+ * (holds A when hidden is NULL, and the prefill path's activation codes).
+ */
+size_t bitlinear_ffn_workspace_bytes(int64_t L, int64_t M, int64_t D, int64_t F);
+
+int bitlinear_ffn_forward(int64_t L, const void* X, int x_dtype, int64_t M, int64_t D, int64_t F,
+                          int64_t D_out, const uint32_t* packed_up, const float* gamma_up,
+                          const uint32_t* packed_down, const float* gamma_down, float* Y,
+                          float* hidden, int path, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* ---- radix-3 weights: five per byte ------------------------------------ */
 /*

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(abi.SIGNATURES)
@@ -82,6 +82,39 @@ def test_r3_checks(lib):
     assert g(1, FAKE, 2, 1, 64, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_DTYPE
     assert g(1, FAKE, 0, 1, 64, P(4104), 8, FAKE, FAKE, None, None) == abi.ERR_ALIGN
     assert g(1, FAKE, 0, 1, 64, FAKE, 8, FAKE, FAKE, P(4098), None) == abi.ERR_ALIGN
+
+
+def test_ffn_checks(lib):
+    f = lib.bitlinear_ffn_forward
+    ws = lib.bitlinear_ffn_workspace_bytes(1, 4, 64, 128)
+    assert ws >= 4 * 128 * 4
+    assert lib.bitlinear_ffn_workspace_bytes(0, 4, 64, 128) == 0
+    #   L, X, dt, M, D, F, Do, pu, gu, pd, gd, Y, hidden, path, ws, ws_bytes, stream
+    args = [1, FAKE, 0, 4, 64, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["L", "X", "dt", "M", "D", "F", "Do", "pu", "gu", "pd", "gd", "Y", "hid", "path", "ws",
+                 "wsb", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(X=None) == abi.ERR_NULL
+    assert call(pd=None) == abi.ERR_NULL
+    assert call(Y=None) == abi.ERR_NULL
+    assert call(L=0) == abi.ERR_SHAPE
+    assert call(F=0) == abi.ERR_SHAPE
+    assert call(Do=-1) == abi.ERR_SHAPE
+    assert call(dt=5) == abi.ERR_DTYPE
+    assert call(path=9) == abi.ERR_ARG
+    assert call(pu=P(4104)) == abi.ERR_ALIGN
+    assert call(hid=P(4100)) == abi.ERR_ALIGN
+    assert call(M=17, path=1) == abi.ERR_SHAPE            # decode forced beyond 16 tokens
+    assert call(ws=None) == abi.ERR_WORKSPACE            # hidden layer needs the workspace
+    assert call(wsb=4 * 128 * 4 - 1) == abi.ERR_WORKSPACE     # decode path: the hidden layer only
+    assert call(path=2, wsb=4 * 128 * 4) == abi.ERR_WORKSPACE  # prefill also holds activation codes
+    assert call(ws=P(4096 + 16)) == abi.ERR_ALIGN
 
 
 def test_status_strings(lib):
