@@ -15,6 +15,9 @@ outputs) against the 8 TB/s HBM3E peak.
 --format radix3 streams the weights packed five per byte (1.6 bits) through
 the same decode kernel; "weights_per_s" compares the two formats.
 
+--workload ffn_block_decode_m8_d2048_f5632 / ffn_block_prefill_m2048_d4096_f11008
+time the BitNet FFN block (BitLinear up -> ReLU^2 -> BitLinear down).
+
 --workload prefill_ffn_m2048_k4096_n11008 (or the 8192x8192x28672 one) times
 the prefill forward instead (activation quantiser + INT8-MFMA GEMM) and
 reports INT8 TOPS (2*M*N*K per step) against the 5.0 POPS dense INT8 peak.
@@ -353,6 +356,116 @@ def cpu_baseline_prefill(P, seconds):
 
 
 # ---------------------------------------------------------------------------
+# BitNet FFN block (BitLinear up -> ReLU^2 -> BitLinear down)
+# ---------------------------------------------------------------------------
+
+FFN_WORKLOADS = {"ffn_block_decode_m8_d2048_f5632": 0.02, "ffn_block_prefill_m2048_d4096_f11008": 0.015}
+
+
+def bench_ffn(args, torch, bl, dev):
+    import numpy as np
+    from bitlinear_absmean_ternarise_bit_amd.workloads import make_ffn_workload
+
+    P = make_ffn_workload(args.workload)
+    sigma = FFN_WORKLOADS[args.workload]
+    M, D, F, Do = P.M, P.D, P.F, P.D_out
+    decode = bl.decode_fits(M, D, F) and bl.decode_fits(M, F, Do)
+    wbytes = F * bl.packed_words(D) * 4 + Do * bl.packed_words(F) * 4
+    L = (args.layers or max(8, -(-(1 << 30) // wbytes))) if decode else 1
+    log(f"[bench] FFN block {args.workload}: M={M} D={D} F={F} D_out={Do}, {L} layer(s), "
+        f"{'decode' if decode else 'prefill'} path")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    X = torch.empty((L, M, D), dtype=torch.bfloat16, device=dev)
+    X[0].copy_(torch.from_numpy(P.X_bf16_bits.view(np.int16)).view(torch.bfloat16))
+    if L > 1:
+        X[1:].copy_(torch.randn((L - 1, M, D), generator=g, device=dev).to(torch.bfloat16))
+        if "outlier_channels" in P.notes:
+            ch = torch.from_numpy(P.notes["outlier_channels"]).to(dev)
+            X[1:, :, ch] = (X[1:, :, ch].float() * 20.0).to(torch.bfloat16)
+    pu = torch.empty((L, F, bl.packed_words(D)), dtype=torch.int32, device=dev)
+    pd = torch.empty((L, Do, bl.packed_words(F)), dtype=torch.int32, device=dev)
+    gu = torch.empty((L,), dtype=torch.float32, device=dev)
+    gd = torch.empty((L,), dtype=torch.float32, device=dev)
+    ws = torch.empty((bl.abi.load().bitlinear_quantize_workspace_bytes(),), dtype=torch.uint8, device=dev)
+    Wu = torch.empty((F, D), dtype=torch.float32, device=dev)
+    Wd = torch.empty((Do, F), dtype=torch.float32, device=dev)
+    for l in range(L):
+        if l == 0:
+            Wu.copy_(torch.from_numpy(P.W_up))
+            Wd.copy_(torch.from_numpy(P.W_down))
+        else:
+            Wu.normal_(0.0, sigma, generator=g)
+            Wd.normal_(0.0, sigma, generator=g)
+        bl.quantize_weights(Wu, out_packed=pu[l], out_gamma=gu[l:l + 1], workspace=ws)
+        bl.quantize_weights(Wd, out_packed=pd[l], out_gamma=gd[l:l + 1], workspace=ws)
+    del Wu, Wd
+    Y = torch.empty((L, M, Do), dtype=torch.float32, device=dev)
+    fws = torch.empty((bl.abi.load().bitlinear_ffn_workspace_bytes(L, M, D, F),), dtype=torch.uint8, device=dev)
+
+    def step():
+        bl.ffn_forward(X, (pu, gu), (pd, gd), out=Y, workspace=fws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    with Timer(torch) as t:
+        for _ in range(args.steps):
+            step()
+    ms_step = t.ms / args.steps
+    ops = 2.0 * 2 * M * D * F * L
+    tops = ops / (ms_step * 1e-3) / 1e12
+    # algorithmic bytes: packed weights, X, the hidden layer written and read, Y
+    step_bytes = L * (wbytes + M * D * 2 + 2 * M * F * 4 + M * Do * 4)
+    gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {gbps:.1f} GB/s, {tops:.1f} TOPS")
+    cfg = {"workload": args.workload + (f" x {L} layers per step (batched decode, cold weights)" if L > 1 else ""),
+           "M": M, "D": D, "F": F, "D_out": Do, "layers": L, "x_dtype": "bf16", "path": "decode" if decode else "prefill",
+           "bytes_per_step": step_bytes, "ops_per_step": ops}
+    if decode:
+        out = {"metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "ms_per_step": round(ms_step, 6),
+               "dtype": "i8", "config": cfg,
+               "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                            "kernel": "decode_kernel x 2 (up with ReLU^2 epilogue, down), one step"}}
+    else:
+        out = {"metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "ms_per_step": round(ms_step, 6),
+               "dtype": "i8", "config": cfg,
+               "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                            "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                            "kernel": "whole block: 2 x (activation quantiser + prefill GEMM)"}}
+    if args.cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_ffn(P, decode, step_bytes // L, args.cpu_seconds)
+    return out
+
+
+def cpu_baseline_ffn(P, decode, layer_bytes, seconds):
+    import numpy as np
+    import oracle as O
+    g_up, q_up, _ = O.quantize_weights(P.W_up)
+    g_dn, q_dn, _ = O.quantize_weights(P.W_down)
+    rows = P.M if decode else 8
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        r0 = (reps * rows) % P.M
+        O.ffn_from_codes(P.X[r0:r0 + rows], q_up, g_up, q_dn, g_dn)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    log(f"[bench] cpu oracle: {reps} blocks of {rows} tokens in {el:.1f} s")
+    if decode:
+        return {"value": round(reps * layer_bytes / el / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+                "kind": "oracle", "sample": f"layer 0 ({P.name}): the oracle's FFN block from ternary codes, "
+                                            f"repeated {reps} times"}
+    ops = 2.0 * 2 * rows * reps * P.D * P.F
+    return {"value": round(ops / el / 1e12, 6), "unit": "TOPS", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{reps * rows} of {P.M} tokens of {P.name}: the oracle's FFN block from ternary codes, "
+                      f"{rows} tokens per call"}
+
+
+# ---------------------------------------------------------------------------
 
 def copy_calibration(torch, dev):
     n = (1 << 30) // 4
@@ -371,7 +484,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_m1_k2048_n2048",
-                    choices=sorted(DECODE_WORKLOADS) + list(PREFILL_WORKLOADS))
+                    choices=sorted(DECODE_WORKLOADS) + list(PREFILL_WORKLOADS) + sorted(FFN_WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="decode pool size (default: >= 1 GiB packed)")
     ap.add_argument("--format", default="2bit", choices=["2bit", "radix3"],
                     help="decode weight format: 2-bit codes or radix-3 (five weights per byte)")
@@ -397,7 +510,9 @@ def main():
     if args.format != "2bit" and args.workload not in DECODE_WORKLOADS:
         print("--format radix3 applies to the decode workloads only", file=sys.stderr)
         sys.exit(2)
-    if args.workload in DECODE_WORKLOADS:
+    if args.workload in FFN_WORKLOADS:
+        out = bench_ffn(args, torch, bl, dev)
+    elif args.workload in DECODE_WORKLOADS:
         out = bench_decode(args, torch, bl, dev)
     else:
         out = bench_prefill(args, torch, bl, dev)

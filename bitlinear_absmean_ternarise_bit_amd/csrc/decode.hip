@@ -256,13 +256,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 }
 
 // Rows per workgroup = 64 * groups.  Larger blocks quantise X less often and
-// stream longer runs; the choice keeps >= 2048 workgroups in flight (8 per
-// CU) when the work allows and wastes at most 1/16 of a layer in its last block.
+// stream longer runs (every workgroup quantises all M tokens, which for long
+// rows costs as much as a few hundred weight rows); the choice keeps >= 512
+// workgroups (2 per CU) when the work allows and wastes at most 1/16 of a
+// layer in its last block.
 int pick_groups(int64_t L, int64_t N) {
   for (int gsz = 16; gsz > 1; gsz >>= 1) {
     const int64_t rows = int64_t(kWaves) * kRowsPerWave * gsz;
     const int64_t bpl = (N + rows - 1) / rows;
-    if (L * bpl >= 2048 && (bpl * rows - N) * 16 <= N) return gsz;
+    if (L * bpl >= 512 && (bpl * rows - N) * 16 <= N) return gsz;
   }
   return 1;
 }
