@@ -501,3 +501,62 @@ def ffn_forward(X: np.ndarray, W_up: np.ndarray, W_down: np.ndarray) -> Dict[str
     out = ffn_from_codes(X, q_up, g_up, q_dn, g_dn)
     out.update({"gamma_up": g_up, "q_up": q_up, "gamma_down": g_dn, "q_down": q_dn})
     return out
+
+
+# ---------------------------------------------------------------------------
+# Backward with the straight-through estimator (STE)
+# [PMV §2, STE paragraph: in the backward pass the gradient of the quantiser is
+# taken as the identity, dW_q/dW = 1, for values inside the valid range;
+# MBC bit_layers.py: BitLinear trains with a straight-through estimator]
+#
+# Reading: the forward is Y = A_hat W_hat^T with A_hat = (gamma_A / 127) A_q
+# and W_hat = gamma W_q.  Both quantisers pass gradients straight through
+# inside their clip ranges: the activation clip [-128, 127] never binds
+# (|x * s| <= 127), and the weight passes where |fp32(W / fp32(gamma + eps))|
+# <= 1 (inside RoundClip), so
+#     dX = dY W_hat,        dW = (dY^T A_hat) * 1[|W / (gamma + eps)| <= 1].
+# gamma and gamma_A are treated as constants.  Gradients and A_hat are in the
+# training precision, bfloat16: dY is given in bfloat16 and A_hat is rounded
+# to bfloat16 from fp32(fp32(gamma_A / 127) * A_q); the contractions here are
+# exact (float64 on these integers-times-bfloat16 products), rounded once.
+# ---------------------------------------------------------------------------
+
+def _to_bf16_values(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bfloat16 (ties to even), returned as float32 values."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def dequant_activations_bf16(Xq: np.ndarray, gamma_a: np.ndarray) -> np.ndarray:
+    """A_hat = bf16(fp32(fp32(gamma_A / 127) * A_q)) as float32 values [M, K]."""
+    c = (np.asarray(gamma_a, np.float32) / np.float32(127.0)).astype(np.float32)
+    a = c[:, None] * np.asarray(Xq).astype(np.float32)
+    assert a.dtype == np.float32
+    return _to_bf16_values(a)
+
+
+def ste_weight_mask(W: np.ndarray, gamma) -> np.ndarray:
+    """1 where the weight lies inside RoundClip's range: |fp32(W / fp32(gamma + eps))| <= 1."""
+    d = np.float32(np.float32(gamma) + EPS32)
+    t = np.asarray(W, np.float32) / d
+    assert t.dtype == np.float32
+    return (np.abs(t) <= np.float32(1.0))
+
+
+def ste_backward(dY: np.ndarray, q: np.ndarray, gamma, Xq: np.ndarray, gamma_a: np.ndarray,
+                 W: np.ndarray) -> Dict[str, np.ndarray]:
+    """dX [M, K] and dW [N, K] (float32) of the forward Y = A_hat W_hat^T under the STE.
+
+    dY: [M, N] bfloat16 values (as float32); q: ternary codes [N, K]; gamma: the
+    weight scale; Xq, gamma_a: the forward's activation codes and scales; W: the
+    float32 weights (for the range mask).
+    """
+    dY = np.asarray(dY, np.float32).astype(np.float64)
+    q64 = np.asarray(q).astype(np.float64)
+    dX = (dY @ q64) * float(np.float32(gamma))
+    A_hat = dequant_activations_bf16(Xq, gamma_a).astype(np.float64)
+    mask = ste_weight_mask(W, gamma)
+    dW = (dY.T @ A_hat) * mask
+    return {"dX": dX.astype(np.float32), "dW": dW.astype(np.float32), "A_hat": A_hat.astype(np.float32),
+            "mask": mask}
