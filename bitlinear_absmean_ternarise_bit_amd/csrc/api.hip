@@ -243,6 +243,46 @@ int bitlinear_ffn_forward(int64_t L, const void* X, int x_dtype, int64_t M, int6
   return BITLINEAR_OK;
 }
 
+int bitlinear_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma, uint32_t* packedT,
+                              void* stream) {
+  if (!W || !gamma || !packedT) return BITLINEAR_ERR_NULL;
+  int st = check_mnk(1, N, K);
+  if (st) return st;
+  st = check_mnk(1, K, N);
+  if (st) return st;
+  if (!aligned(W, 4) || !aligned(gamma, 4) || !aligned(packedT, 16)) return BITLINEAR_ERR_ALIGN;
+  return hip_status(launch_pack_transposed(W, N, K, gamma, packedT, static_cast<hipStream_t>(stream)));
+}
+
+size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  return backward_workspace_bytes(M, N, K);
+}
+
+int bitlinear_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, const uint32_t* packedT,
+                       const float* gamma, const int8_t* Xq, const float* gamma_a, const float* W, float* dX,
+                       float* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dY || !gamma || (!dX && !dW)) return BITLINEAR_ERR_NULL;
+  if (dX && !packedT) return BITLINEAR_ERR_NULL;
+  if (dW && (!Xq || !gamma_a || !W)) return BITLINEAR_ERR_NULL;
+  int st = check_mnk(M, N, K);
+  if (st) return st;
+  st = check_mnk(M, K, N);
+  if (st) return st;
+  // bf16 operands are addressed with 32-bit byte offsets
+  const int64_t Mp = ((M + 63) / 64) * 64;
+  const int64_t lim = int64_t(1) << 31;
+  if (M * padded_k(N) * 2 >= lim || N * Mp * 2 >= lim || K * Mp * 2 >= lim) return BITLINEAR_ERR_SHAPE;
+  if (!aligned(dY, 2) || !aligned(gamma, 4) || (packedT && !aligned(packedT, 16)) ||
+      (gamma_a && !aligned(gamma_a, 4)) || (W && !aligned(W, 4)) || (dX && !aligned(dX, 4)) ||
+      (dW && !aligned(dW, 4)))
+    return BITLINEAR_ERR_ALIGN;
+  if (!workspace || workspace_bytes < backward_workspace_bytes(M, N, K)) return BITLINEAR_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITLINEAR_ERR_ALIGN;
+  return hip_status(launch_backward(dY, M, N, K, packedT, gamma, Xq, gamma_a, W, dX, dW, workspace,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 int64_t bitlinear_r3_padded_k(int64_t K) { return K < 1 ? 0 : r3_padded_k(K); }
 
 size_t bitlinear_r3_packed_bytes(int64_t N, int64_t K) {

@@ -45,4 +45,12 @@ hipError_t launch_prefill_gemm(const int8_t* Xq, const float* gamma_a, const int
                                const float* gamma, float* Y, int32_t* acc, hipStream_t stream,
                                bool relu2 = false);
 
+// STE backward: codes of W^T (2-bit format, rows k) and the two bf16 GEMMs
+hipError_t launch_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma, uint32_t* packedT,
+                                  hipStream_t stream);
+size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, const uint32_t* packedT,
+                           const float* gamma, const int8_t* Xq, const float* gamma_a, const float* W, float* dX,
+                           float* dW, void* workspace, hipStream_t stream);
+
 }  // namespace bitlinear

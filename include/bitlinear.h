@@ -240,6 +240,47 @@ int bitlinear_ffn_forward(int64_t L, const void* X, int x_dtype, int64_t M, int6
                           float* hidden, int path, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* ---- backward with the straight-through estimator ----------------------- */
+/*
+ * [PMV s2, its STE passage]: the quantiser's gradient is taken as the identity
+ * inside the valid range.  With the forward Y = A_hat W_hat^T,
+ * A_hat = (gamma_A / 127) A_q and W_hat = gamma W_q:
+ *   dX = dY W_hat = gamma (dY W_q)                          [M, K]
+ *   dW = (dY^T A_hat) * 1[|fp32(W / fp32(gamma + eps))| <= 1]  [N, K]
+ * (the activation clip never binds; gamma, gamma_A are constants).  Training
+ * precision: dY is bfloat16, A_hat = bf16(fp32(fp32(gamma_A/127) * A_q)) (round
+ * half to even), products on bf16 matrix cores with float32 accumulation, so
+ * results differ from exact sums by float32 accumulation rounding.
+ */
+
+/* Codes of W^T for the backward's dX: the same ternary codes (same gamma,
+ * computed by bitlinear_quantize_weights on W) transposed, as a [K, N] matrix
+ * in the 2-bit packed format of this file (bitlinear_packed_bytes(K, N) bytes).
+ * W: device float32 [N, K]; gamma: device float32[1]; packedT: device,
+ * 16-byte aligned. */
+int bitlinear_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma,
+                              uint32_t* packedT, void* stream);
+
+/* Workspace bytes of bitlinear_backward: padded and transposed bf16 copies of
+ * dY and A_hat (about 2 M (2N + K) bytes). */
+size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * dY: device bfloat16 [M, N] (bit patterns), the gradient of Y.
+ * packedT: from bitlinear_pack_transposed (needed for dX).
+ * Xq, gamma_a: the forward's activation codes [M, Kp] and scales [M], as
+ *   bitlinear_quantize_activations writes them (needed for dW).
+ * W: device float32 [N, K], the weights the codes came from (for dW's mask).
+ * dX: device float32 [M, K] or NULL;  dW: device float32 [N, K] or NULL
+ *   (at least one).  workspace: >= bitlinear_backward_workspace_bytes(M, N, K),
+ *   256-byte aligned.  Requires M*padded_k(N), N*M and K*M (M rounded up to 64)
+ *   below 2^30.
+ */
+int bitlinear_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K,
+                       const uint32_t* packedT, const float* gamma,
+                       const int8_t* Xq, const float* gamma_a, const float* W,
+                       float* dX, float* dW, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- radix-3 weights: five per byte ------------------------------------ */
 /*
  * The Radix-3 packing of [PMV s4] (the section on how bitnet.cpp speeds up CPU

@@ -1,0 +1,136 @@
+"""STE backward on the GPU (through the C ABI) against the oracle.
+
+Bit-exact: the transposed packed codes and the positions where dW is masked to
+zero.  dX and dW: the products dY * code and dY * A_hat are exact in float32
+and the GPU sums them in float32 (bf16 matrix cores), so each result may differ
+from the oracle's exact sum by at most L * 2^-24 * sum|products| (L = the
+contraction length, one rounding per addition) plus one final rounding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bitlinear_absmean_ternarise_bit_amd as bl
+import oracle as O
+from bitlinear_absmean_ternarise_bit_amd import abi
+from bitlinear_absmean_ternarise_bit_amd.workloads import f32_to_bf16_bits, bf16_bits_to_f32, random_problem
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def bound_check(got, ref, absprod, L):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    tol = L * 2.0 ** -24 * absprod + 2.0 ** -23 * np.abs(ref)
+    bad = np.abs(got - ref) > tol
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"mismatch at {idx.tolist()}: gpu {got[tuple(idx.T)]} ref {ref[tuple(idx.T)]}")
+    # rounding errors stay far below the worst case: a dropped or misplaced
+    # product (about sum|products| / L) would show in the median
+    nz = absprod > 0
+    if nz.any():
+        med = float(np.median(np.abs(got - ref)[nz] / absprod[nz]))
+        assert med < 2.0 ** -20, med
+
+
+def setup(M, K, N, seed, outside=0.1):
+    rng = np.random.default_rng(seed)
+    P = random_problem(M, K, N, seed=seed, x_dtype="bf16")
+    W = P.W.copy()
+    W[rng.random(W.shape) < outside] *= 4.0  # weights outside the clip range: masked gradient
+    bits = f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    dY = bf16_bits_to_f32(bits)
+    Wd = torch.from_numpy(W).to(DEV)
+    packed, gamma = bl.quantize_weights(Wd)
+    X = torch.from_numpy(P.X_bf16_bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    Xq, ga, _ = bl.quantize_activations(X)
+    packedT = bl.pack_transposed(Wd, gamma)
+    dYd = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return P, W, dY, Wd, gamma, Xq, ga, packedT, dYd
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (70, 33), (129, 300), (640, 1000), (16, 4097)])
+def test_pack_transposed_bit_exact(N, K):
+    say(f"pack_transposed N={N} K={K}")
+    P = random_problem(1, K, N, seed=N * K)
+    W = torch.from_numpy(P.W).to(DEV)
+    packed, gamma = bl.quantize_weights(W)
+    pT = bl.pack_transposed(W, gamma)
+    torch.cuda.synchronize()
+    g, q, _ = O.quantize_weights(P.W)
+    assert pT.shape == (K, bl.packed_words(N))
+    assert np.array_equal(pT.cpu().numpy().view(np.uint32), O.pack_codes(np.ascontiguousarray(q.T)))
+
+
+BWD_CASES = [(1, 64, 64), (37, 300, 130), (128, 256, 192), (200, 1000, 520), (65, 130, 1100), (300, 64, 7)]
+
+
+@pytest.mark.parametrize("M,K,N", BWD_CASES)
+def test_backward_parity(M, K, N):
+    say(f"backward M={M} K={K} N={N}")
+    P, W, dY, Wd, gamma, Xq, ga, packedT, dYd = setup(M, K, N, seed=M + K + N)
+    dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, Wd)
+    torch.cuda.synchronize()
+    g, q, _ = O.quantize_weights(W)
+    rga, rxq, _ = O.absmax_quantize(P.X)
+    assert np.array_equal(Xq.cpu().numpy()[:, :K], rxq)
+    ref = O.ste_backward(dY, q, g, rxq, rga, W)
+    absX = (np.abs(dY).astype(np.float64) @ np.abs(q).astype(np.float64)) * float(g)
+    bound_check(dX.cpu().numpy(), ref["dX"], absX, N)
+    absW = np.abs(dY).astype(np.float64).T @ np.abs(ref["A_hat"]).astype(np.float64)
+    got_w = dW.cpu().numpy()
+    assert np.all(got_w[~ref["mask"]] == 0.0)
+    bound_check(got_w, ref["dW"], absW, M)
+
+
+def test_backward_one_output_at_a_time():
+    P, W, dY, Wd, gamma, Xq, ga, packedT, dYd = setup(50, 200, 90, seed=7)
+    dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, Wd)
+    dX1, n1 = bl.backward(dYd, packedT, gamma, Xq, ga, Wd, need_dw=False)
+    n2, dW2 = bl.backward(dYd, packedT, gamma, Xq, ga, Wd, need_dx=False)
+    torch.cuda.synchronize()
+    assert n1 is None and n2 is None
+    assert torch.equal(dX, dX1) and torch.equal(dW, dW2)
+
+
+def test_backward_7b_ffn_shape_sampled():
+    # the 7B-like prefill projection (2048 x 4096 -> 11008): sampled rows of dX and dW
+    M, K, N = 2048, 4096, 11008
+    say(f"backward {M}x{K}x{N} (sampled)")
+    P, W, dY, Wd, gamma, Xq, ga, packedT, dYd = setup(M, K, N, seed=11, outside=0.05)
+    dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, Wd)
+    torch.cuda.synchronize()
+    g, q, _ = O.quantize_weights(W)
+    rga, rxq, _ = O.absmax_quantize(P.X)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([rng.choice(M, 24, replace=False), [0, M - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(N, 24, replace=False), [0, N - 1]]))
+    # dX rows depend on dY rows only; dW rows (output channels) on dY columns only
+    refx = O.ste_backward(dY[rows], q, g, rxq[rows], rga[rows], W)["dX"]
+    absX = (np.abs(dY[rows]).astype(np.float64) @ np.abs(q).astype(np.float64)) * float(g)
+    bound_check(dX.cpu().numpy()[rows], refx, absX, N)
+    refw = O.ste_backward(dY[:, cols], q[cols], g, rxq, rga, W[cols])
+    absW = np.abs(dY[:, cols]).astype(np.float64).T @ np.abs(refw["A_hat"]).astype(np.float64)
+    got_w = dW.cpu().numpy()[cols]
+    assert np.all(got_w[~refw["mask"]] == 0.0)
+    bound_check(got_w, refw["dW"], absW, M)
+
+
+def test_backward_errors():
+    lib = abi.load()
+    z = torch.zeros((4, 4), dtype=torch.bfloat16, device=DEV)
+    g = torch.ones((1,), device=DEV)
+    assert lib.bitlinear_backward(z.data_ptr(), 4, 4, 4, None, g.data_ptr(), None, None, None, None, None,
+                                  None, 0, None) == abi.ERR_NULL
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.backward(z, torch.zeros((4, 4), dtype=torch.int32, device=DEV), g,
+                    torch.zeros((4, 64), dtype=torch.int8, device=DEV), g.repeat(4),
+                    torch.zeros((4, 4), device=DEV), workspace=torch.empty((16,), dtype=torch.uint8, device=DEV))
+    assert e.value.status == abi.ERR_WORKSPACE
