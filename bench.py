@@ -18,6 +18,9 @@ the same decode kernel; "weights_per_s" compares the two formats.
 --workload ffn_block_decode_m8_d2048_f5632 / ffn_block_prefill_m2048_d4096_f11008
 time the BitNet FFN block (BitLinear up -> ReLU^2 -> BitLinear down).
 
+--workload ste_backward_m2048_k4096_n11008 times the STE backward (dX and dW)
+of the 7B-like projection in bf16 TFLOP/s.
+
 --workload prefill_ffn_m2048_k4096_n11008 (or the 8192x8192x28672 one) times
 the prefill forward instead (activation quantiser + INT8-MFMA GEMM) and
 reports INT8 TOPS (2*M*N*K per step) against the 5.0 POPS dense INT8 peak.
@@ -466,6 +469,86 @@ def cpu_baseline_ffn(P, decode, layer_bytes, seconds):
 
 
 # ---------------------------------------------------------------------------
+# STE backward (dX and dW of one BitLinear)
+# ---------------------------------------------------------------------------
+
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+BACKWARD_WORKLOADS = {"ste_backward_m2048_k4096_n11008": "prefill_ffn_m2048_k4096_n11008"}
+
+
+def bench_backward(args, torch, bl, dev):
+    import numpy as np
+    from bitlinear_absmean_ternarise_bit_amd.workloads import make_workload
+
+    P = make_workload(BACKWARD_WORKLOADS[args.workload])
+    M, K, N = P.M, P.K, P.N
+    log(f"[bench] STE backward {args.workload}: M={M} K={K} N={N} (dX and dW, bf16 gradients)")
+    W = torch.from_numpy(P.W).to(dev)
+    packed, gamma = bl.quantize_weights(W)
+    X = torch.from_numpy(P.X_bf16_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    Xq, ga, _ = bl.quantize_activations(X)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    dY = torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16)
+    packedT = torch.empty((K, bl.packed_words(N)), dtype=torch.int32, device=dev)
+    with Timer(torch) as tp:
+        bl.pack_transposed(W, gamma, out=packedT)
+    ws = torch.empty((bl.abi.load().bitlinear_backward_workspace_bytes(M, N, K),), dtype=torch.uint8, device=dev)
+
+    def step():
+        bl.backward(dY, packedT, gamma, Xq, ga, W, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    with Timer(torch) as t:
+        for _ in range(args.steps):
+            step()
+    ms_step = t.ms / args.steps
+    flops = 2.0 * 2 * M * N * K
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
+    out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms_step, 6),
+           "dtype": "bf16",
+           "config": {"workload": args.workload, "M": M, "K": K, "N": N, "flops_per_step": flops,
+                      "note": "dX = gamma dY W_q and dW = (dY^T A_hat) * range mask, bf16 matrix cores"},
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "bf16_gemm_nt_kernel x 2 + operand preparation, one step"},
+           "pack_transposed": {"ms": round(tp.ms, 4), "note": "codes of W^T, once per weight update"}}
+    if args.cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(P, args.cpu_seconds)
+    return out
+
+
+def cpu_baseline_backward(P, seconds):
+    import numpy as np
+    import oracle as O
+    from bitlinear_absmean_ternarise_bit_amd.workloads import f32_to_bf16_bits, bf16_bits_to_f32
+    g, q, _ = O.quantize_weights(P.W)
+    gA, Xq, _ = O.absmax_quantize(P.X)
+    dY = bf16_bits_to_f32(f32_to_bf16_bits(np.random.default_rng(0).standard_normal((P.M, 64)).astype(np.float32)))
+    rows = 8
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        r0 = (reps * rows) % P.M
+        # dX for `rows` tokens (all N) and dW for 64 output channels (all M)
+        dYr = bf16_bits_to_f32(f32_to_bf16_bits(np.random.default_rng(reps).standard_normal((rows, P.N))
+                                                .astype(np.float32)))
+        O.ste_backward(dYr, q, g, Xq[r0:r0 + rows], gA[r0:r0 + rows], P.W)
+        O.ste_backward(dY, q[:64], g, Xq, gA, P.W[:64])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    flops = reps * (2.0 * rows * P.N * P.K + 2.0 * 64 * P.M * P.K)
+    log(f"[bench] cpu oracle: {reps} samples in {el:.1f} s")
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{reps} x (dX of {rows} tokens + dW of 64 output channels) of {P.M}x{P.K}x{P.N}"}
+
+
+# ---------------------------------------------------------------------------
 
 def copy_calibration(torch, dev):
     n = (1 << 30) // 4
@@ -484,7 +567,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_m1_k2048_n2048",
-                    choices=sorted(DECODE_WORKLOADS) + list(PREFILL_WORKLOADS) + sorted(FFN_WORKLOADS))
+                    choices=sorted(DECODE_WORKLOADS) + list(PREFILL_WORKLOADS) + sorted(FFN_WORKLOADS)
+                    + sorted(BACKWARD_WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="decode pool size (default: >= 1 GiB packed)")
     ap.add_argument("--format", default="2bit", choices=["2bit", "radix3"],
                     help="decode weight format: 2-bit codes or radix-3 (five weights per byte)")
@@ -510,7 +594,9 @@ def main():
     if args.format != "2bit" and args.workload not in DECODE_WORKLOADS:
         print("--format radix3 applies to the decode workloads only", file=sys.stderr)
         sys.exit(2)
-    if args.workload in FFN_WORKLOADS:
+    if args.workload in BACKWARD_WORKLOADS:
+        out = bench_backward(args, torch, bl, dev)
+    elif args.workload in FFN_WORKLOADS:
         out = bench_ffn(args, torch, bl, dev)
     elif args.workload in DECODE_WORKLOADS:
         out = bench_decode(args, torch, bl, dev)

@@ -11,7 +11,8 @@
 //
 // Both contractions run on one bf16 MFMA GEMM, C[p, q] = sum_r A[p, r] B[q, r],
 // whose operands both have the contraction index contiguous:
-//   dX: A = dY (a zero-padded copy), B = the ternary codes of W^T, packed in
+//   dX: A = dY (in place when its rows start on 16-byte boundaries, else a
+//       zero-padded copy), B = the ternary codes of W^T, packed in
 //       the 2-bit format (pack_transposed_kernel) and expanded to bf16 {-1,0,1}
 //       while they are staged into LDS;
 //   dW: A = dY^T, B = A_hat^T (transposed copies, zero-padded along M).
@@ -117,15 +118,19 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
 }
 
 // bf16 MFMA GEMM, C[p, q] = sum_r A[p, r] B[q, r] over r < Rp (a multiple of 64).
-// A: bf16 [P, Rp].  B: bf16 [Q, Rp] (BMODE 0) or the 2-bit ternary codes of a
-// [Q, Rp] matrix in the packed format (BMODE 1), expanded to bf16 c - 1.
+// A: bf16 [P, Rp] with row stride lda >= Rp, or, when B is packed, lda >= the
+// number of real columns (padding codes are zero weights, so whatever A holds
+// past a row's end only meets zeros); rows 16-byte aligned.  B: bf16 [Q, Rp]
+// (BMODE 0) or the 2-bit ternary codes of a [Q, Rp] matrix in the packed
+// format (BMODE 1), expanded to bf16 c - 1.
 // EPI 0: C * gamma;  EPI 1: C where |fp32(W[p, q] / fp32(gamma + eps))| <= 1, else 0.
 // Tile 128 x 128, 4 waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32), 64 r per
 // LDS stage, two stages; rows of an operand stage are 128 bytes with 16-byte
 // slot c of row r stored at slot c ^ (r & 7).
 template <int BMODE, int EPI>
 __global__ __launch_bounds__(256) void bf16_gemm_nt_kernel(const uint16_t* __restrict__ A, int64_t P,
-                                                           const void* __restrict__ B, int64_t Q, int64_t Rp,
+                                                           int64_t lda, const void* __restrict__ B, int64_t Q,
+                                                           int64_t Rp,
                                                            float* __restrict__ C, int64_t ldc,
                                                            const float* __restrict__ gamma,
                                                            const float* __restrict__ W, int64_t ldw,
@@ -144,6 +149,7 @@ __global__ __launch_bounds__(256) void bf16_gemm_nt_kernel(const uint16_t* __res
   const int64_t q0 = static_cast<int64_t>(blockIdx.x) * BN;
   const int niter = static_cast<int>(Rp / BK);
   const uint32_t rowbytes = static_cast<uint32_t>(Rp) * 2u;
+  const uint32_t rowbytes_a = static_cast<uint32_t>(lda) * 2u;
 
   const __amdgpu_buffer_rsrc_t rsrc_a =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0, bytes_a, 0x00020000);
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(256) void bf16_gemm_nt_kernel(const uint16_t* __res
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s = tid + 256 * i, r = s >> 3, c = s & 7;
-    a_off[i] = (p0 + r < P) ? static_cast<uint32_t>(p0 + r) * rowbytes + 16u * c : kOff;
+    a_off[i] = (p0 + r < P) ? static_cast<uint32_t>(p0 + r) * rowbytes_a + 16u * c : kOff;
     b_off[i] = (q0 + r < Q) ? static_cast<uint32_t>(q0 + r) * rowbytes + 16u * c : kOff;
     a_dst[i] = r * ROWB + 16 * (c ^ (r & 7));
   }
@@ -300,12 +306,17 @@ hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, 
   ws += align256(static_cast<size_t>(N * Mp * 2));
   uint16_t* At = reinterpret_cast<uint16_t*>(ws);
   if (dX) {
-    int64_t blocks = (M * Np + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    pad_rows_bf16_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(dY, M, N, dYp, Np);
+    // dY's rows serve as they are when they start on 16-byte boundaries
+    const bool direct = N % 8 == 0 && reinterpret_cast<uintptr_t>(dY) % 16 == 0;
+    if (!direct) {
+      int64_t blocks = (M * Np + 255) / 256;
+      if (blocks > 65536) blocks = 65536;
+      pad_rows_bf16_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(dY, M, N, dYp, Np);
+    }
     const dim3 grid(static_cast<unsigned>((K + 127) / 128), static_cast<unsigned>((M + 127) / 128));
-    bf16_gemm_nt_kernel<1, 0><<<grid, 256, 0, stream>>>(dYp, M, packedT, K, Np, dX, K, gamma, nullptr, 0,
-                                                         static_cast<int>(M * Np * 2),
+    bf16_gemm_nt_kernel<1, 0><<<grid, 256, 0, stream>>>(direct ? dY : dYp, M, direct ? N : Np, packedT, K, Np,
+                                                         dX, K, gamma, nullptr, 0,
+                                                         static_cast<int>(M * (direct ? N : Np) * 2),
                                                          static_cast<int>(K * (Np / 4)));
   }
   if (dW) {
@@ -314,7 +325,7 @@ hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, 
     const dim3 g1(static_cast<unsigned>((K + kTile - 1) / kTile), static_cast<unsigned>(Mp / kTile));
     transpose_kernel<1><<<g1, 256, 0, stream>>>(Xq, M, K, Kp, gamma_a, At, Mp);
     const dim3 grid(static_cast<unsigned>((K + 127) / 128), static_cast<unsigned>((N + 127) / 128));
-    bf16_gemm_nt_kernel<0, 1><<<grid, 256, 0, stream>>>(dYt, N, At, K, Mp, dW, K, gamma, W, K,
+    bf16_gemm_nt_kernel<0, 1><<<grid, 256, 0, stream>>>(dYt, N, Mp, At, K, Mp, dW, K, gamma, W, K,
                                                          static_cast<int>(N * Mp * 2),
                                                          static_cast<int>(K * Mp * 2));
   }
