@@ -8,7 +8,7 @@
  * (add/subtract/skip, INT32 accumulation, rescale by gamma_A * gamma / 127),
  * [PMV s3] the section on the memory wall (2-bit packing, 0.25 byte/weight),
  * [PMV s4] the section on how bitnet.cpp speeds up inference on CPUs (the
- * LUT figure and the Radix-3 packing of five weights per byte), [PMV s5] its
+ * LUT figure and the Radix-3 packing of five weights per byte), [PMV s6] its
  * section on trade-offs and engineering challenges.
  *
  * Conventions shared by every entry point
@@ -213,7 +213,7 @@ int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, 
  *   Y_l = BitLinear_down(A_l)          (packed_down: [D_out, F], gamma_down[l]);
  *         A_l is quantised per token with AbsMax like any BitLinear input [PMV s1]
  * [MBC] is the shadowgraph.io page on a multimodal architecture around
- * bitnet.cpp.  Norms stay outside, in floating point [PMV s5: the trade-offs
+ * bitnet.cpp.  Norms stay outside, in floating point [PMV s6: the trade-offs
  * section].  H is formed in float32 exactly as every output here
  * (fp32(acc) * fp32(fp32(gamma * gamma_A) / 127)) and A = fp32(r * r), r = max(H, 0).
  *

@@ -22,7 +22,7 @@ quantisation, the BitLinear layer and Zero-GEMM).  Its sections:
 * [PMV §3]  the memory wall: 2-bit packing, 0.25 byte per weight;
 * [PMV §4]  how bitnet.cpp speeds up CPU inference: the 81-entry LUT figure
   for four weights and the Radix-3 packing of five weights per byte;
-* [PMV §5]  the trade-offs section: attention, SwiGLU-style activations and
+* [PMV §6]  the trade-offs section: attention, SwiGLU-style activations and
   RMSNorm stay in floating point (or INT8).
 
 [MBC] is the shadowgraph.io page on a hybrid multimodal architecture around
@@ -450,7 +450,7 @@ def sampled_forward(X: np.ndarray, q: np.ndarray, gamma, rows, cols) -> Dict[str
 
 # ---------------------------------------------------------------------------
 # BitNet FFN block: BitLinear up -> ReLU^2 -> BitLinear down
-# [MBC bit_layers.py: ReLU^2 activation; PMV §5: non-linear parts in floating
+# [MBC bit_layers.py: ReLU^2 activation; PMV §6: non-linear parts in floating
 # point; PMV §1 AbsMax: each BitLinear quantises its own input per token]
 #
 # Reading: the block is Y = BitLinear_down(ReLU^2(BitLinear_up(X))) with no
