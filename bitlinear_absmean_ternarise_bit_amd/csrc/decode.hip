@@ -108,6 +108,15 @@ __device__ __forceinline__ void unit_operands(const uint4& r, v4i (&bop)[Format<
 // activation of a BitNet FFN block).
 enum Epilogue { kEpiY = 0, kEpiAcc = 1, kEpiRelu2 = 2 };
 
+// Outputs of a wave (M tokens x 16 * groups rows, 4 bytes each, twice with
+// the accumulators) are staged in LDS and stored once at the end when they
+// take at most 4 KiB per wave and the workgroup's LDS stays within 64 KiB;
+// otherwise each row group stores directly.
+__host__ __device__ inline int stage_bytes(int M, int groups, bool with_acc, int64_t code_bytes) {
+  const int b = M * groups * kRowsPerWave * 4 * (with_acc ? 2 : 1);
+  return (M * groups * kRowsPerWave * 4 <= 4096 && code_bytes + kWaves * b <= 65536) ? b : 0;
+}
+
 template <int FMT, int DT, bool VEC, int EPI>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const void* __restrict__ X, int M, int64_t K, int64_t Kp, int64_t units,
@@ -124,6 +133,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const int64_t layer = blockIdx.x / blocks_per_layer;
   const int rb = static_cast<int>(blockIdx.x - layer * blocks_per_layer);
   const int64_t lds_stride = Kp + 16;  // +16 bytes: token rows start on different banks
+  const int stage = stage_bytes(M, groups, EPI == kEpiAcc, M * lds_stride);  // per wave, 0: direct stores
   X = static_cast<const char*>(X) + layer * M * K * esize;
   packed += layer * N * units * 4;
   Y += layer * M * N;
@@ -201,10 +211,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const v4i zero = {0, 0, 0, 0};
   const float gm = gamma[0];
   v4i c = zero;
+  // the lane's output tokens 4g + r are fixed: their code sums and rescale
+  // factors gamma * gamma_A / 127 are formed once, not per row group
+  int tok_rs[4];
+  float tok_scale[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * g + r;
+    const int ic = i < M ? i : M - 1;
+    tok_rs[r] = s_rs[ic];
+    tok_scale[r] = __fdiv_rn(__fmul_rn(gm, s_ga[ic]), 127.0f);
+  }
 
-  auto contract = [&](int b, const uint4 (&r)[kUnroll]) {
-    const int gi = b / bpg;
-    const int cb = b - gi * bpg;
+  auto mfma_batch = [&](int b, const uint4 (&r)[kUnroll]) {
+    const int cb = b - (b / bpg) * bpg;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint32_t un = static_cast<uint32_t>(cb * kUnroll + u) * 4u + g;
@@ -219,40 +239,80 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop[t], c, 0, 0, 0);
       }
     }
-    // epilogue of the row group after its last batch: lane holds tokens
-    // 4g + r of weight row n
-    const bool last = cb == bpg - 1;
-    const uint32_t n = static_cast<uint32_t>(n_base + gi * kRowsPerWave + j);
+  };
+
+  // Staging area of this wave: out_y[i][x] (token i, row x of the wave's
+  // 16 * groups rows), then out_acc likewise.
+  const int wave_rows = groups * kRowsPerWave;
+  float* out_y = reinterpret_cast<float*>(sxq + M * lds_stride) + wave * (stage / 4);
+  int* out_acc = reinterpret_cast<int*>(out_y + M * wave_rows);
+
+  // After the last batch of a row group: rescale (lane holds tokens 4g + r
+  // of weight row n), stage or store, and clear the accumulator.  Reading
+  // the accumulator waits for the group's chain of MFMAs; the caller issues
+  // the next loads first, so two batches stay in flight meanwhile.
+  auto epilogue = [&](int b) {
+    const int gi = b / bpg;
+    if (b - gi * bpg != bpg - 1) return;
+    const int x = gi * kRowsPerWave + j;
+    const uint32_t n = static_cast<uint32_t>(n_base + x);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * g + r;
-      const int ic = i < M ? i : M - 1;
-      const int v = c[r] - s_rs[ic];
-      const float scale = __fdiv_rn(__fmul_rn(gm, s_ga[ic]), 127.0f);
-      float y = __fmul_rn(static_cast<float>(v), scale);
+      const int v = c[r] - tok_rs[r];
+      float y = __fmul_rn(static_cast<float>(v), tok_scale[r]);
       if constexpr (EPI == kEpiRelu2) {
-        const float r = fmaxf(y, 0.0f);
-        y = __fmul_rn(r, r) + 0.0f;  // + 0: no negative zero
+        const float rl = fmaxf(y, 0.0f);
+        y = __fmul_rn(rl, rl) + 0.0f;  // + 0: no negative zero
       }
-      const uint32_t off = (last && i < M && n < N32) ? (static_cast<uint32_t>(i) * N32 + n) * 4u : kOff;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), ysrc, off, 0, 0);
-      if constexpr (EPI == kEpiAcc) __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(v), asrc, off, 0, 0);
+      if (stage) {
+        if (i < M) {
+          out_y[i * wave_rows + x] = y;
+          if constexpr (EPI == kEpiAcc) out_acc[i * wave_rows + x] = v;
+        }
+      } else {
+        const uint32_t off = (i < M && n < N32) ? (static_cast<uint32_t>(i) * N32 + n) * 4u : kOff;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), ysrc, off, 0, 0);
+        if constexpr (EPI == kEpiAcc) __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(v), asrc, off, 0, 0);
+      }
     }
-    c = last ? zero : c;
+    c = zero;
   };
 
-  // sched_barrier keeps the scheduler from sinking a batch's loads into the
-  // contraction that follows them.
+  // Batch b is in buf(b % 2); batch b + 1 is in flight while b is contracted,
+  // and the loads of b + 2 go out (into b's buffer, whose codes are already
+  // unpacked) before b's epilogue.  sched_barrier keeps the scheduler from
+  // sinking loads into the work that follows them.
+  load_batch(1, 1 < nbatch, buf1);
+  __builtin_amdgcn_sched_barrier(0);
   int b = 0;
   for (; b + 1 < nbatch; b += 2) {
-    load_batch(b + 1, true, buf1);
-    __builtin_amdgcn_sched_barrier(0);
-    contract(b, buf0);
+    mfma_batch(b, buf0);
     load_batch(b + 2, b + 2 < nbatch, buf0);
     __builtin_amdgcn_sched_barrier(0);
-    contract(b + 1, buf1);
+    epilogue(b);
+    mfma_batch(b + 1, buf1);
+    load_batch(b + 3, b + 3 < nbatch, buf1);
+    __builtin_amdgcn_sched_barrier(0);
+    epilogue(b + 1);
   }
-  if (b < nbatch) contract(b, buf0);
+  if (b < nbatch) {
+    mfma_batch(b, buf0);
+    epilogue(b);
+  }
+  if (stage) {
+    // the wave's outputs, row-contiguous per token; LDS operations of one
+    // wave complete in order, so the staged values are visible here
+    for (int i = 0; i < M; ++i) {
+      for (int x = lane; x < wave_rows; x += kWave) {
+        const uint32_t n = static_cast<uint32_t>(n_base + x);
+        const uint32_t off = n < N32 ? (static_cast<uint32_t>(i) * N32 + n) * 4u : kOff;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out_y[i * wave_rows + x]), ysrc, off, 0, 0);
+        if constexpr (EPI == kEpiAcc)
+          __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(out_acc[i * wave_rows + x]), asrc, off, 0, 0);
+      }
+    }
+  }
 }
 
 // Rows per workgroup = 64 * groups.  Larger blocks quantise X less often and
@@ -279,8 +339,11 @@ hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed,
   const int64_t rows = int64_t(kWaves) * kRowsPerWave * groups;
   const int bpl = static_cast<int>((N + rows - 1) / rows);
   const unsigned blocks = static_cast<unsigned>(L * bpl);
-  const size_t lds = static_cast<size_t>(M) * static_cast<size_t>(Kp + 16);
   const int m = static_cast<int>(M);
+  const bool with_acc = acc != nullptr && !relu2;
+  const int64_t code_bytes = M * (Kp + 16);
+  const size_t lds = static_cast<size_t>(code_bytes) +
+                     static_cast<size_t>(kWaves) * stage_bytes(m, groups, with_acc, code_bytes);
   if constexpr (FMT == 2) {
     if (relu2) {
       decode_kernel<FMT, DT, VEC, kEpiRelu2><<<blocks, kDecodeThreads, lds, stream>>>(
