@@ -12,6 +12,12 @@
 // Tiling: a workgroup of WM x WN waves owns a BM (tokens) x BN (weight rows)
 // output tile; each wave owns a (BM/WM) x (BN/WN) sub-tile made of 32 x 32
 // MFMA tiles (256 x 256 with 4 x 2 waves for large problems).  K advances 128 per stage through two LDS stages.
+// Workgroups are persistent, one per CU: each walks every gridDim.x-th tile,
+// and requests the next tile's first stage before it writes the finished
+// tile's outputs.  The per-row dequantisation terms (gamma * gamma_A / 127 and
+// the token code sum) of a tile are formed once, by one thread per row, into
+// LDS, so the epilogue issues no global loads (a load there would wait for the
+// stores before it: vector-memory completions are counted in order).
 // Global loads run two stages ahead into two register sets (buffer loads with
 // 32-bit offsets; rows past M or N read as zeros from the hardware bounds
 // check), and the stage after the one being contracted is written to LDS
@@ -32,6 +38,7 @@
 // 16 activation codes at k = 16 w(s, h) of its token row: the same k on both
 // sides.  Steps 0 and 1 use words 0..3 only, so a final half stage (Kp not a
 // multiple of 128) just skips steps 2 and 3.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -70,27 +77,33 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
   constexpr bool B_ALL = B_SLOTS >= THREADS;  // else only threads < B_SLOTS load packed words
   static_assert(A_LOADS >= 1 && MI >= 1 && NI >= 1, "tile too small for the workgroup");
   __shared__ __align__(1024) char smem[2 * STAGE];
+  // dequantisation terms of the current tile's rows: gamma * gamma_A / 127 and
+  // the token code sum
+  __shared__ float row_scale[BM];
+  __shared__ int row_sum[BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // Workgroup -> tile.  Workgroups are dealt round-robin to the 8 XCDs; give
-  // each XCD a contiguous run of tiles, walked in groups of 8 tile rows so the
-  // tiles resident on one XCD share activation and weight panels in its L2.
+  // Tile index -> tile.  Workgroups are dealt round-robin to the 8 XCDs and
+  // each walks the tiles t = blockIdx.x + gridDim.x i (gridDim.x is a multiple
+  // of 8 or covers every tile), so a workgroup stays on one XCD; give each XCD
+  // a contiguous run of tiles, walked in groups of 8 tile rows so the tiles
+  // resident on one XCD share activation and weight panels in its L2.
   const int num_tiles = tiles_m * tiles_n;
-  int t = blockIdx.x;
-  if (num_tiles % 8 == 0) t = (t & 7) * (num_tiles >> 3) + (t >> 3);
   constexpr int GROUP = 8;
-  const int group = t / (GROUP * tiles_n);
-  const int first_m = group * GROUP;
-  const int gsize = min(tiles_m - first_m, GROUP);
-  const int in_group = t - group * GROUP * tiles_n;
-  const int tm = first_m + in_group % gsize;
-  const int tn = in_group / gsize;
-  const int64_t m0 = static_cast<int64_t>(tm) * BM;
-  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  int64_t m0 = 0, n0 = 0;
+  auto place = [&](int t) {
+    if (num_tiles % 8 == 0) t = (t & 7) * (num_tiles >> 3) + (t >> 3);
+    const int group = t / (GROUP * tiles_n);
+    const int first_m = group * GROUP;
+    const int gsize = min(tiles_m - first_m, GROUP);
+    const int in_group = t - group * GROUP * tiles_n;
+    m0 = static_cast<int64_t>(first_m + in_group % gsize) * BM;
+    n0 = static_cast<int64_t>(in_group / gsize) * BN;
+  };
 
   // Global sources: buffer resources over the whole code arrays, 32-bit lane
   // offsets; rows past M or N fall outside the resource and read as zeros
@@ -106,18 +119,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
   // tid + THREADS q is row (tid >> 1) + (THREADS / 2) q, half tid & 1
   const int a_r = tid >> 3, a_c = tid & 7;
   const int b_r = tid >> 1, b_c = tid & 1;
-  const uint32_t voff_a = static_cast<uint32_t>(m0 + a_r) * kp32 + 16u * a_c;
   const uint32_t a_row_step = (THREADS / 8) * kp32;          // rows of activation codes per q
-  // packed row b_n in the interleaved row order (see unit_offset): block base,
-  // row within the block, rows of the block
   static_assert(B_LOADS == 1, "one packed slot per thread per stage");
+  static_assert(BM <= THREADS, "one thread per tile row loads its dequantisation terms");
   const uint32_t units = kp32 >> 6;
   const uint32_t N32 = static_cast<uint32_t>(N);
-  const uint32_t b_n = static_cast<uint32_t>(n0 + b_r);
-  const bool b_ok = b_n < N32;
-  const uint32_t b_blk = (b_n & ~15u) * units * 16u;
-  const uint32_t b_j = b_n & 15u;
-  const uint32_t b_R = b_ok ? min(16u, N32 - (b_n & ~15u)) : 0u;
+  // per-tile source offsets: the activation slot, and packed row b_n in the
+  // interleaved row order (see unit_offset): block base, row within the
+  // block, rows of the block
+  uint32_t voff_a = 0, b_blk = 0, b_j = 0, b_R = 0;
+  bool b_ok = false;
+  int row_rs = 0;
+  float row_ga = 0.0f;
+  auto set_tile = [&](int t) {
+    place(t);
+    voff_a = static_cast<uint32_t>(m0 + a_r) * kp32 + 16u * a_c;
+    const uint32_t b_n = static_cast<uint32_t>(n0 + b_r);
+    b_ok = b_n < N32;
+    b_blk = (b_n & ~15u) * units * 16u;
+    b_j = b_n & 15u;
+    b_R = b_ok ? min(16u, N32 - (b_n & ~15u)) : 0u;
+    const int64_t m = m0 + tid;
+    if (tid < BM && m < M) {
+      row_rs = rowsum[m];
+      row_ga = gamma_a[m];
+    }
+  };
   // LDS destinations (swizzled)
   int a_dst[A_LOADS], b_dst[B_LOADS];  // b_dst: LDS offset of the slot's first 8-byte half
 #pragma unroll
@@ -161,12 +188,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
   };
 
   v16i c[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) c[mi][ni][r] = 0;
 
   const int lr = lane & 31;
   const int lh = lane >> 5;
@@ -217,68 +238,102 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
-  // prologue: stage 0 -> LDS 0; stage 1 in register set 1; stage 2 loading into set 0
+  const float gm = gamma[0];
+  int t = blockIdx.x;
+  set_tile(t);
   gload(0, S0());
   gload(min(1, niter - 1), S1());
-  swrite(smem, S0());
-  gload(min(2, niter - 1), S0());
-  __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-
-  // Iteration it contracts LDS stage it % 2; halfway it writes stage it + 1
-  // (register set (it + 1) % 2, loaded two iterations earlier) into the other
-  // LDS stage and reloads that register set with stage it + 3.  Past the last
-  // stage the write lands in the idle LDS stage and the reload repeats the last
-  // stage: harmless, and the loop stays free of branches, which keeps the
-  // compiler's count of outstanding loads exact (it then waits only for the
-  // older register set).
-  auto iteration = [&](int it, auto set_tag) {
-    const char* cur = smem + (it & 1) * STAGE;
-    char* nxt = smem + ((it + 1) & 1) * STAGE;
-    contract_half(cur, 0);
-    swrite(nxt, set_tag);
-    gload(min(it + 3, niter - 1), set_tag);
-    contract_half(cur, 1);
+  for (;;) {
+    // Prologue: stage 0 -> LDS 0; stage 1 in register set 1; stage 2 loading
+    // into set 0.  Stages 0 and 1 were requested before the previous tile's
+    // epilogue, and every wave is past that epilogue's LDS reads.
+    swrite(smem, S0());
+    if (tid < BM) {
+      row_scale[tid] = __fdiv_rn(__fmul_rn(gm, row_ga), 127.0f);
+      row_sum[tid] = row_rs;
+    }
+    gload(min(2, niter - 1), S0());
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[mi][ni][r] = 0;
     __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");  // LDS traffic stays on its side of the barrier
-  };
-  int it = 0;
-  for (; it + 1 < nfull; it += 2) {
-    iteration(it, S1());
-    iteration(it + 1, S0());
-  }
-  if (it < nfull) iteration(it, S1());
-  if (nfull < niter) contract_half(smem + (nfull & 1) * STAGE, 0);  // final half stage
+    asm volatile("" ::: "memory");
 
-  // epilogue: lane holds rows 8*(r/4) + 4*(l/32) + r%4, column l%32 of each 32x32 tile
-  const float gm = gamma[0];
+    // Iteration it contracts LDS stage it % 2; halfway it writes stage it + 1
+    // (register set (it + 1) % 2, loaded two iterations earlier) into the
+    // other LDS stage and reloads that register set with stage it + 3.  Past
+    // the last stage the write lands in the idle LDS stage and the reload
+    // repeats the last stage: harmless, and the loop stays free of branches,
+    // which keeps the compiler's count of outstanding loads exact (it then
+    // waits only for the older register set).
+    auto iteration = [&](int it, auto set_tag) {
+      const char* cur = smem + (it & 1) * STAGE;
+      char* nxt = smem + ((it + 1) & 1) * STAGE;
+      contract_half(cur, 0);
+      swrite(nxt, set_tag);
+      gload(min(it + 3, niter - 1), set_tag);
+      contract_half(cur, 1);
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");  // LDS traffic stays on its side of the barrier
+    };
+    int it = 0;
+    for (; it + 1 < nfull; it += 2) {
+      iteration(it, S1());
+      iteration(it + 1, S0());
+    }
+    if (it < nfull) iteration(it, S1());
+    if (nfull < niter) contract_half(smem + (nfull & 1) * STAGE, 0);  // final half stage
+
+    // Request the next tile's first stage and row terms, so they arrive while
+    // this tile's outputs are written.
+    const int64_t em0 = m0, en0 = n0;
+    const int tn = t + static_cast<int>(gridDim.x);
+    const bool more = tn < num_tiles;
+    if (more) {
+      set_tile(tn);
+      gload(0, S0());
+    }
+
+    // epilogue: lane holds rows 8*(r/4) + 4*(l/32) + r%4, column l%32 of each 32x32 tile
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t m = m0 + wm * (BM / WM) + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-      if (m >= M) continue;
-      const int rs = rowsum[m];
-      const float scale = __fdiv_rn(__fmul_rn(gm, gamma_a[m]), 127.0f);
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * (BM / WM) + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int64_t m = em0 + row;
+        if (m >= M) continue;
+        const int rs = row_sum[row];
+        const float scale = row_scale[row];
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int64_t n = n0 + wn * (BN / WN) + ni * 32 + lr;
-        if (n < N) {
-          const int v = c[mi][ni][r] - rs;
-          if constexpr (EPI == 1) acc[m * ldy + n] = v;
-          float y = __fmul_rn(static_cast<float>(v), scale);
-          if constexpr (EPI == 2) {
-            const float r = fmaxf(y, 0.0f);
-            y = __fmul_rn(r, r) + 0.0f;  // + 0: no negative zero
+        for (int ni = 0; ni < NI; ++ni) {
+          const int64_t n = en0 + wn * (BN / WN) + ni * 32 + lr;
+          if (n < N) {
+            const int v = c[mi][ni][r] - rs;
+            if constexpr (EPI == 1) acc[m * ldy + n] = v;
+            float y = __fmul_rn(static_cast<float>(v), scale);
+            if constexpr (EPI == 2) {
+              const float r = fmaxf(y, 0.0f);
+              y = __fmul_rn(r, r) + 0.0f;  // + 0: no negative zero
+            }
+            Y[m * ldy + n] = y;
           }
-          Y[m * ldy + n] = y;
         }
       }
     }
+    if (!more) break;
+    t = tn;
+    gload(min(1, niter - 1), S1());
+    __builtin_amdgcn_s_barrier();  // every wave is done with this tile's LDS
+    asm volatile("" ::: "memory");
   }
 }
+
+constexpr int64_t kCUs = 256;  // compute units of an MI355X: one workgroup each
 
 // Rows [0, N) of the packed matrix against the tokens; Y and acc have row
 // stride ldy (N when the launch covers all output columns).
@@ -293,7 +348,8 @@ hipError_t launch_tile(const int8_t* Xq, const float* gamma_a, const int32_t* ro
     const int64_t Mc = min(M - r0, chunk);
     const int tiles_m = static_cast<int>((Mc + BM - 1) / BM);
     const int tiles_n = static_cast<int>((N + BN - 1) / BN);
-    const unsigned blocks = static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n);
+    // persistent workgroups, one per CU, each walking every gridDim.x-th tile
+    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>(int64_t(tiles_m) * tiles_n, kCUs));
     const int bytes_a = static_cast<int>(Mc * Kp);
     if (relu2)
       prefill_gemm_kernel<BM, BN, WM, WN, 2><<<blocks, 64 * WM * WN, 0, stream>>>(
@@ -312,8 +368,6 @@ hipError_t launch_tile(const int8_t* Xq, const float* gamma_a, const int32_t* ro
   }
   return hipSuccess;
 }
-
-constexpr int64_t kCUs = 256;  // compute units of an MI355X: one workgroup each
 
 }  // namespace
 
