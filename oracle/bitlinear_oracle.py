@@ -48,6 +48,10 @@ Readings where the article leaves a step open:
   multiple of 64 weights with c = 1 (a zero weight); row n is a run of
   little-endian 32-bit words, word j covers k in [16j, 16j + 16), and bits
   [8b + 2i, 8b + 2i + 1] of word j hold the code of k = 16j + 4i + b.
+* The LUT contraction (a comparison to the matrix-core path) takes blocks of
+  four consecutive activations; its table index is the base-3 number of the
+  block's codes c = q + 1, first weight most significant, which is the digit
+  order the LUT figure's rows 0 / 40 / 80 fix.
 * Both packed formats (2-bit and radix-3) cut each row into 16-byte units and
   store the units of 16 consecutive rows interleaved: see
   :func:`interleave_units`.
@@ -560,3 +564,88 @@ def ste_backward(dY: np.ndarray, q: np.ndarray, gamma, Xq: np.ndarray, gamma_a: 
     dW = (dY.T @ A_hat) * mask
     return {"dX": dX.astype(np.float32), "dW": dW.astype(np.float32), "A_hat": A_hat.astype(np.float32),
             "mask": mask}
+
+
+# ---------------------------------------------------------------------------
+# LUT GEMV (the CPU prior art, as a comparison)  [PMV §4, LUT-GEMM figure]
+# ---------------------------------------------------------------------------
+
+LUT_GROUP = 4     # activations per table
+LUT_ENTRIES = 81  # 3**4 sign patterns of four ternary weights
+
+
+def lut_index(c4) -> int:
+    """Table index of four weight codes c_t = q_t + 1: the base-3 number c_0 c_1 c_2 c_3.
+
+    c_0 is the most significant digit, which puts all -1 at index 0, all 0 at
+    40 and all +1 at 80, the three rows the LUT figure prints.
+    """
+    idx = 0
+    for c in c4:
+        c = int(c)
+        if c not in (0, 1, 2):
+            raise ValueError("lut_index: code outside {0, 1, 2}")
+        idx = 3 * idx + c
+    return idx
+
+
+def lut_digits(idx: int):
+    """The four base-3 digits (c_0 first) of a table index in [0, 81)."""
+    if not 0 <= idx < LUT_ENTRIES:
+        raise ValueError("lut_digits: index outside [0, 81)")
+    out = []
+    for _ in range(LUT_GROUP):
+        out.append(idx % 3)
+        idx //= 3
+    return out[::-1]
+
+
+def lut_table(a4) -> np.ndarray:
+    """The 81 pre-sums of four INT8 activations: T[idx] = sum_t (c_t - 1) * a_t (int64 [81])."""
+    a = [int(x) for x in a4]
+    if len(a) != LUT_GROUP:
+        raise ValueError("lut_table: needs four activations")
+    T = np.empty(LUT_ENTRIES, np.int64)
+    for idx in range(LUT_ENTRIES):
+        T[idx] = sum((c - 1) * x for c, x in zip(lut_digits(idx), a))
+    return T
+
+
+def lut_gemv(Xq: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """acc = A_q x W_q^T formed the LUT way: one 81-entry table per token and block of 4 activations.
+
+    K is split into blocks of 4 consecutive positions (the last one padded with
+    zero activations and zero weights).  For every token and block the table
+    of pre-sums is built once; every weight row then reads, per block, the
+    entry its four codes index, and the entries are summed in INT32.
+    """
+    Xq = np.asarray(Xq, np.int64)
+    q = np.asarray(q, np.int64)
+    M, K = Xq.shape
+    N = q.shape[0]
+    Kg = -(-K // LUT_GROUP) * LUT_GROUP
+    G = Kg // LUT_GROUP
+    Xp = np.zeros((M, Kg), np.int64)
+    Xp[:, :K] = Xq
+    cp = np.ones((N, Kg), np.int64)  # code 1 = weight 0 in the padding
+    cp[:, :K] = q + 1
+    if cp.min(initial=1) < 0 or cp.max(initial=1) > 2:
+        raise ValueError("lut_gemv: weights not ternary")
+    idx = np.zeros((N, G), np.int64)
+    for t in range(LUT_GROUP):  # base-3 number of the block's codes, c_0 first
+        idx = 3 * idx + cp[:, t::LUT_GROUP]
+    acc = np.zeros((M, N), np.int64)
+    blocks = np.arange(G)
+    for m in range(M):
+        tables = np.stack([lut_table(Xp[m, LUT_GROUP * g:LUT_GROUP * (g + 1)]) for g in range(G)])
+        acc[m] = tables[blocks[None, :], idx].sum(axis=1)
+    if acc.size and (acc.min() < -(1 << 31) or acc.max() >= (1 << 31)):
+        raise OverflowError("lut_gemv: INT32 accumulator overflow")
+    return acc
+
+
+def lut_forward(X: np.ndarray, q: np.ndarray, gamma) -> Dict[str, np.ndarray]:
+    """Forward with the LUT contraction: quantise tokens, lut_gemv, dequantise."""
+    gA, Xq, rowsum = absmax_quantize(X)
+    acc = lut_gemv(Xq, q)
+    return {"gamma_a": gA, "Xq": Xq, "rowsum": rowsum, "acc": acc, "Y": dequant(acc, gamma, gA)}
