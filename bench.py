@@ -13,7 +13,9 @@ HBM).  The metric is GB/s of algorithmic bytes (packed weights + activations +
 outputs) against the 8 TB/s HBM3E peak.
 
 --format radix3 streams the weights packed five per byte (1.6 bits) through
-the same decode kernel; "weights_per_s" compares the two formats.
+the same decode kernel; "weights_per_s" compares the two formats.  --format
+lut contracts the same 2-bit weights through 81-entry LDS tables per block of
+four activations (the CPU LUT scheme, as a comparison).
 
 --workload ffn_block_decode_m8_d2048_f5632 / ffn_block_prefill_m2048_d4096_f11008
 time the BitNet FFN block (BitLinear up -> ReLU^2 -> BitLinear down).
@@ -71,6 +73,7 @@ TRAFFIC = {
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "quant_act.hpp", "common.hpp"],
     "prefill": ["prefill.hip", "common.hpp"],
+    "lut": ["lut.hip", "common.hpp"],
 }
 
 
@@ -183,6 +186,7 @@ def bench_decode(args, torch, bl, dev):
     from bitlinear_absmean_ternarise_bit_amd.workloads import make_workload
 
     r3 = args.format == "radix3"
+    lut = args.format == "lut"
     P0 = make_workload(args.workload)
     M, K, N = P0.M, P0.K, P0.N
     row_bytes = bl.r3_row_bytes(K) if r3 else bl.packed_words(K) * 4
@@ -191,12 +195,21 @@ def bench_decode(args, torch, bl, dev):
     log(f"[bench] decode {args.workload} ({args.format}): M={M} K={K} N={N}, pool of {L} layers "
         f"({L * packed_bytes / 2**30:.2f} GiB packed)")
     # weights: quantisation is offline, not part of the step; timed separately
-    P, X, packed, gamma, tq_ms, _ = build_decode_pool(torch, bl, dev, args.workload, L, args.format)
+    P, X, packed, gamma, tq_ms, _ = build_decode_pool(torch, bl, dev, args.workload, L,
+                                                      "radix3" if r3 else "2bit")
     Y = torch.empty((L, M, N), dtype=torch.float32, device=dev)
     wq_bytes = L * (4 * N * K + packed_bytes)
     log(f"[bench] weight quantisation of {L} layers: {tq_ms:.1f} ms")
 
-    if r3:
+    if lut:
+        ws = torch.empty((bl.lut_workspace_bytes(L, M, K),), dtype=torch.uint8, device=dev)
+
+        def step():
+            bl.forward_lut(X, packed, gamma, K, out=Y, workspace=ws)
+
+        def single(l, out):
+            bl.forward_lut(X[l], packed[l], gamma[l:l + 1], K, out=out, workspace=ws)
+    elif r3:
         def step():
             bl.forward_r3(X, packed, gamma, K, out=Y)
 
@@ -241,11 +254,15 @@ def bench_decode(args, torch, bl, dev):
         "config": {"workload": f"{args.workload} x {L} layers per step (batched decode, cold weights)",
                    "M": M, "K": K, "N": N, "layers": L, "x_dtype": "bf16",
                    "weight_format": "radix-3, 5 weights per byte" if r3 else "2-bit",
+                   "contraction": "81-entry LUTs in LDS (comparison variant)" if lut else "INT8 MFMA",
                    "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_for(args.workload + ("/radix3" if r3 else ""), "decode"),
-                     "kernel": "decode_kernel (fused quantise + GEMV + rescale), one launch per step"},
+                     "traffic": traffic_for(args.workload + ("/radix3" if r3 else "/lut" if lut else ""),
+                                            "lut" if lut else "decode"),
+                     "kernel": ("lut_gemv_kernel (tables + lookups + rescale) after act_quant_kernel, two "
+                                "launches per step" if lut else
+                                "decode_kernel (fused quantise + GEMV + rescale), one launch per step")},
         "weights_per_s": {"value": round(gw_s, 2), "unit": "G weights/s",
                           "note": "N*K*layers per step / step time: compares weight formats"},
         "single_call": {"us": round(single_us, 2), "GBps": round(layer_bytes / (single_us * 1e-6) / 1e9, 2),
@@ -256,16 +273,17 @@ def bench_decode(args, torch, bl, dev):
                                 "note": "absmean + ternarise + pack, offline, not in the step"},
     }
     if args.cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_decode(P, layer_bytes, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline_decode(P, layer_bytes, args.cpu_seconds, lut)
     return out
 
 
-def cpu_baseline_decode(P, layer_bytes, seconds):
+def cpu_baseline_decode(P, layer_bytes, seconds, lut=False):
     import oracle as O
     gamma, q, _ = O.quantize_weights(P.W)
+    fwd = O.lut_forward if lut else O.forward_from_codes
     reps, t0 = 0, time.perf_counter()
     while True:
-        O.forward_from_codes(P.X, q, gamma)
+        fwd(P.X, q, gamma)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -274,7 +292,8 @@ def cpu_baseline_decode(P, layer_bytes, seconds):
     return {"value": round(reps * layer_bytes / el / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
             "kind": "oracle",
             "sample": f"layer 0 of the pool ({P.name}, seed 0): the oracle's forward from ternary "
-                      f"codes (absmax quantise + exact contraction + rescale) repeated {reps} times"}
+                      f"codes (absmax quantise + {'LUT' if lut else 'exact'} contraction + rescale) "
+                      f"repeated {reps} times"}
 
 
 # ---------------------------------------------------------------------------
@@ -574,8 +593,9 @@ def main():
                     choices=sorted(DECODE_WORKLOADS) + list(PREFILL_WORKLOADS) + sorted(FFN_WORKLOADS)
                     + sorted(BACKWARD_WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="decode pool size (default: >= 1 GiB packed)")
-    ap.add_argument("--format", default="2bit", choices=["2bit", "radix3"],
-                    help="decode weight format: 2-bit codes or radix-3 (five weights per byte)")
+    ap.add_argument("--format", default="2bit", choices=["2bit", "radix3", "lut"],
+                    help="decode weight format: 2-bit codes or radix-3 (five weights per byte); "
+                         "lut: 2-bit codes contracted through 81-entry tables (comparison)")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -596,7 +616,7 @@ def main():
         copy_calibration(torch, dev)
         return
     if args.format != "2bit" and args.workload not in DECODE_WORKLOADS:
-        print("--format radix3 applies to the decode workloads only", file=sys.stderr)
+        print("--format radix3 / lut apply to the decode workloads only", file=sys.stderr)
         sys.exit(2)
     if args.workload in BACKWARD_WORKLOADS:
         out = bench_backward(args, torch, bl, dev)

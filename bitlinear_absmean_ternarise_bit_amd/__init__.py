@@ -315,6 +315,55 @@ def forward_r3(X, packed, gamma, K: int | None = None, return_acc: bool = False,
     return (Y, acc) if return_acc else Y
 
 
+# ---- LUT contraction (comparison variant) ----------------------------------
+
+def lut_workspace_bytes(L: int, M: int, K: int) -> int:
+    return int(abi.load().bitlinear_lut_workspace_bytes(L, M, K))
+
+
+def forward_lut(X, packed, gamma, K: int | None = None, return_acc: bool = False, out=None, workspace=None):
+    """Decode forward through 81-entry LUTs over 2-bit weights (a comparison to ``forward``).
+
+    X [M, K] with packed [N, words] and gamma [1], or X [L, M, K] with
+    packed [L, N, words] and gamma [L].  Returns Y float32 [M, N] / [L, M, N]
+    (and the INT32 accumulators if asked).
+    """
+    torch = _torch()
+    for t, nm in ((X, "X"), (packed, "packed"), (gamma, "gamma")):
+        _require_cuda(t, nm)
+    batched = X.dim() == 3
+    if batched:
+        if packed.dim() != 3:
+            raise ValueError("X [L, M, K] needs packed [L, N, words]")
+        L, M, Kx = X.shape
+        N = packed.shape[1]
+        if packed.shape[0] != L or gamma.numel() != L:
+            raise ValueError("inconsistent batched shapes")
+    else:
+        if X.dim() != 2 or packed.dim() != 2:
+            raise ValueError("X must be [M, K] and packed [N, words]")
+        L = 1
+        M, Kx = X.shape
+        N = packed.shape[0]
+    K = Kx if K is None else K
+    if K != Kx:
+        raise ValueError("K does not match X")
+    if packed.shape[-1] != packed_words(K):
+        raise ValueError("packed does not hold padded_k(K) // 16 words per row")
+    lib = abi.load()
+    ws_bytes = int(lib.bitlinear_lut_workspace_bytes(L, M, K))
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=X.device)
+    shape = (L, M, N) if batched else (M, N)
+    Y = out if out is not None else torch.empty(shape, dtype=torch.float32, device=X.device)
+    acc = torch.empty(shape, dtype=torch.int32, device=X.device) if return_acc else None
+    abi.check("bitlinear_forward_lut",
+              lib.bitlinear_forward_lut(L, _ptr(X), _x_dtype(X), M, K, _ptr(packed), N, _ptr(gamma),
+                                        _ptr(Y), _ptr(acc), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(X)))
+    return (Y, acc) if return_acc else Y
+
+
 # ---- the BitNet FFN block --------------------------------------------------
 
 def ffn_forward(X, up, down, path: str = "auto", return_hidden: bool = False, out=None, workspace=None):

@@ -54,6 +54,8 @@ SIGNATURES = {
     "bitlinear_r3_packed_bytes": (_sz, [_i64, _i64]),
     "bitlinear_quantize_weights_r3": (_int, [_p, _i64, _i64, _p, _p, _p, _sz, _p]),
     "bitlinear_forward_r3": (_int, [_i64, _p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _p]),
+    "bitlinear_lut_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bitlinear_forward_lut": (_int, [_i64, _p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _p, _sz, _p]),
     "bitlinear_status_string": (ctypes.c_char_p, [_int]),
 }
 

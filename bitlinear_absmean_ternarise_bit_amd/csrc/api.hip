@@ -320,6 +320,33 @@ int bitlinear_forward_r3(int64_t L, const void* X, int x_dtype, int64_t M, int64
                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t bitlinear_lut_workspace_bytes(int64_t L, int64_t M, int64_t K) {
+  if (L < 1 || M < 1 || K < 1 || L > (int64_t(1) << 20) || M > kDecodeMaxM) return 0;
+  return prefill_ws_bytes(L * M, K);
+}
+
+int bitlinear_forward_lut(int64_t L, const void* X, int x_dtype, int64_t M, int64_t K,
+                          const uint32_t* packed, int64_t N, const float* gamma, float* Y, int32_t* acc,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!X || !packed || !gamma || !Y) return BITLINEAR_ERR_NULL;
+  if (L < 1 || L > (int64_t(1) << 20)) return BITLINEAR_ERR_SHAPE;
+  if (M < 1 || M > kDecodeMaxM) return BITLINEAR_ERR_SHAPE;
+  int st = check_mnk(L * M, N, K);
+  if (st) return st;
+  if (L * ((N + 255) / 256) >= (int64_t(1) << 31)) return BITLINEAR_ERR_SHAPE;
+  st = check_x(X, x_dtype);
+  if (st) return st;
+  if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(Y, 4) || (acc && !aligned(acc, 4)))
+    return BITLINEAR_ERR_ALIGN;
+  if (!workspace || workspace_bytes < prefill_ws_bytes(L * M, K)) return BITLINEAR_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITLINEAR_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PrefillWs w = prefill_ws(workspace, L * M, K);
+  hipError_t e = launch_act_quant(X, x_dtype, L * M, K, w.xq, w.ga, w.rs, s);
+  if (e != hipSuccess) return BITLINEAR_ERR_HIP;
+  return hip_status(launch_lut_gemv(w.xq, w.ga, M, K, packed, N, gamma, Y, acc, L, s));
+}
+
 const char* bitlinear_status_string(int status) {
   switch (status) {
     case BITLINEAR_OK: return "ok";

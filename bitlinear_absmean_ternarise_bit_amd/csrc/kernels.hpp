@@ -45,6 +45,11 @@ hipError_t launch_prefill_gemm(const int8_t* Xq, const float* gamma_a, const int
                                const float* gamma, float* Y, int32_t* acc, hipStream_t stream,
                                bool relu2 = false);
 
+// LUT contraction (comparison variant): codes from launch_act_quant for L
+// layers of M <= kDecodeMaxM tokens (rows l * M .. l * M + M - 1), 2-bit weights
+hipError_t launch_lut_gemv(const int8_t* Xq, const float* gamma_a, int64_t M, int64_t K, const uint32_t* packed,
+                           int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L, hipStream_t stream);
+
 // STE backward: codes of W^T (2-bit format, rows k) and the two bf16 GEMMs
 hipError_t launch_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma, uint32_t* packedT,
                                   hipStream_t stream);

@@ -329,6 +329,41 @@ int bitlinear_forward_r3(int64_t L, const void* X, int x_dtype, int64_t M, int64
                          const uint8_t* packed, int64_t N, const float* gamma,
                          float* Y, int32_t* acc, void* stream);
 
+/* ---- LUT contraction: the CPU prior art, kept as a comparison ---------- */
+/*
+ * [PMV s4] (the LUT-GEMM figure) contracts a block of four INT8 activations
+ * with four ternary weights by reading one of 81 pre-computed sums, indexed by
+ * the weights' base-3 pattern (index 0 = all -1, 40 = all 0, 80 = all +1).
+ * These calls run that scheme on the GPU over the ordinary 2-bit weights: a
+ * workgroup builds the 81-entry tables of its tokens in LDS for a slice of K
+ * and every thread looks up, per packed byte (four weights), one entry per
+ * token.  The accumulators are the exact INT32 sums of every other path.  It
+ * is slower than the matrix-core decode GEMV and is not chosen by
+ * bitlinear_forward; it exists to measure the two schemes side by side.
+ */
+
+/* Workspace of bitlinear_forward_lut: the codes, scales and code sums of
+ * L*M tokens (as bitlinear_forward_workspace_bytes(L*M, K)); 0 on bad sizes. */
+size_t bitlinear_lut_workspace_bytes(int64_t L, int64_t M, int64_t K);
+
+/*
+ * LUT forward(s) over 2-bit weights: for l = 0..L-1,
+ *   Y_l = (Xq_l x q_l^T) * gamma[l] * gamma_A / 127              [PMV s2, s4]
+ * Layer l reads X + l*M*K elements (dtype x_dtype), the packed matrix at
+ * packed + l*bitlinear_packed_bytes(N, K) bytes and gamma[l], and writes
+ * Y + l*M*N (and acc + l*M*N when acc is not NULL).  Two launches: the
+ * per-token AbsMax quantiser over the L*M tokens, then the LUT kernel.
+ * Requires 1 <= M <= bitlinear_max_decode_m(), 1 <= L <= 2^20,
+ * L*ceil(N/256) < 2^31; packed 16-byte aligned, Y and acc 4-byte aligned,
+ * workspace device memory of bitlinear_lut_workspace_bytes(L, M, K) bytes,
+ * 256-byte aligned.
+ * Errors: BITLINEAR_ERR_NULL, _SHAPE, _DTYPE, _ALIGN, _WORKSPACE, _HIP.
+ */
+int bitlinear_forward_lut(int64_t L, const void* X, int x_dtype, int64_t M, int64_t K,
+                          const uint32_t* packed, int64_t N, const float* gamma,
+                          float* Y, int32_t* acc, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* bitlinear_status_string(int status);
 

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(abi.SIGNATURES)
@@ -82,6 +82,39 @@ def test_r3_checks(lib):
     assert g(1, FAKE, 2, 1, 64, FAKE, 8, FAKE, FAKE, None, None) == abi.ERR_DTYPE
     assert g(1, FAKE, 0, 1, 64, P(4104), 8, FAKE, FAKE, None, None) == abi.ERR_ALIGN
     assert g(1, FAKE, 0, 1, 64, FAKE, 8, FAKE, FAKE, P(4098), None) == abi.ERR_ALIGN
+
+
+def test_lut_checks(lib):
+    assert lib.bitlinear_lut_workspace_bytes(3, 8, 100) == lib.bitlinear_forward_workspace_bytes(24, 100)
+    assert lib.bitlinear_lut_workspace_bytes(1, 17, 100) == 0   # at most 16 tokens
+    assert lib.bitlinear_lut_workspace_bytes(0, 1, 100) == 0
+    f = lib.bitlinear_forward_lut
+    ws = lib.bitlinear_lut_workspace_bytes(2, 4, 64)
+    #   L, X, dt, M, K, packed, N, gamma, Y, acc, ws, ws_bytes, stream
+    args = [2, FAKE, 1, 4, 64, FAKE, 8, FAKE, FAKE, None, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["L", "X", "dt", "M", "K", "packed", "N", "gamma", "Y", "acc", "ws", "wsb", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(X=None) == abi.ERR_NULL
+    assert call(packed=None) == abi.ERR_NULL
+    assert call(Y=None) == abi.ERR_NULL
+    assert call(L=0) == abi.ERR_SHAPE
+    assert call(M=0) == abi.ERR_SHAPE
+    assert call(M=17) == abi.ERR_SHAPE
+    assert call(N=0) == abi.ERR_SHAPE
+    assert call(K=(1 << 20) + 1) == abi.ERR_SHAPE
+    assert call(dt=7) == abi.ERR_DTYPE
+    assert call(X=P(4097)) == abi.ERR_ALIGN
+    assert call(packed=P(4104)) == abi.ERR_ALIGN
+    assert call(acc=P(4098)) == abi.ERR_ALIGN
+    assert call(ws=None) == abi.ERR_WORKSPACE
+    assert call(wsb=ws - 1) == abi.ERR_WORKSPACE
+    assert call(ws=P(4096 + 16)) == abi.ERR_ALIGN
 
 
 def test_ffn_checks(lib):
