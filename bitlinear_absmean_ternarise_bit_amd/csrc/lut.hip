@@ -16,14 +16,16 @@
 // entry e holds sum_t (c_t(e) - 1) a_t, at most 4 * 127 in magnitude (int16).
 //
 // A workgroup owns 256 weight rows of one layer (a thread per row) and walks
-// K in slices of 128 weights (two 16-byte units per row, 32 blocks): it builds
-// the 32 tables of each token for the slice, then every thread reads its
-// row's two units, turns each byte into a table index with SWAR arithmetic
-// and adds one table entry per token.  The accumulators stay in registers and
-// the epilogue applies the same rescale as the other paths.  The tables cost
-// 81 entries per block per token per workgroup, so this variant pays off only
-// when a workgroup's 256 rows share them; the lookups are LDS reads, one per
-// block per token, which bounds it well below the matrix-core GEMV.
+// K in slices of 256 weights (128 for 5 to 8 tokens, 64 beyond, so a slice
+// has at most 256 tables): it builds each token's tables for the slice, a
+// thread per table, then every thread turns its row's packed bytes of the
+// slice into table indices with SWAR arithmetic and adds one table entry per
+// token.  Rows are read 64 contiguous bytes (four units) at a time, so no
+// line is fetched twice.  The accumulators stay in registers and the epilogue
+// applies the same rescale as the other paths.  The tables cost 81 entries
+// per block per token per workgroup, paid back only because a workgroup's
+// 256 rows share them; the lookups are LDS reads, one per block per token,
+// which bounds the scheme well below the matrix-core GEMV as M grows.
 #include "kernels.hpp"
 
 namespace bitlinear {
@@ -31,7 +33,6 @@ namespace bitlinear {
 namespace {
 
 constexpr int kLutRows = 256;    // weight rows per workgroup, one per thread
-constexpr int kLutBlocks = 32;   // blocks of four weights per slice (128 weights)
 constexpr int kLutStride = 41;   // 32-bit words per table: 81 int16 entries + 1 pad
 
 // Index bytes of four packed-code bytes: per byte, the base-3 number of its
@@ -66,14 +67,17 @@ __device__ __forceinline__ void build_table(uint32_t* table, int a0, int a1, int
     table[p] = (static_cast<uint32_t>(e[2 * p]) & 0xffffu) | (static_cast<uint32_t>(e[2 * p + 1]) << 16);
 }
 
-// M tokens (<= 16); the tables of token m, block g start at word
-// (m * 32 + g) * 41 of LDS.
+// M tokens (<= 16).  A slice is SU 16-byte units of every row (16 SU blocks);
+// the tables of token m, block g of the slice start at word (m * 16 SU + g) * 41
+// of LDS.  Rows are read a chunk of four units (64 contiguous bytes) at a time.
 template <int M>
 __global__ __launch_bounds__(kLutRows) void lut_gemv_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ gamma_a, int64_t Kp,
     const uint32_t* __restrict__ packed, int64_t N, const float* __restrict__ gamma, float* __restrict__ Y,
     int32_t* __restrict__ acc_out, int blocks_per_layer) {
-  __shared__ uint32_t tables[M * kLutBlocks * kLutStride];
+  constexpr int SU = M <= 4 ? 4 : M <= 8 ? 2 : 1;  // units per slice: at most 256 tables, 42 KB of LDS
+  constexpr int G = 16 * SU;          // blocks per slice
+  __shared__ uint32_t tables[M * G * kLutStride];
   const int tid = threadIdx.x;
   const int64_t layer = blockIdx.x / blocks_per_layer;
   const uint32_t n = static_cast<uint32_t>(blockIdx.x % blocks_per_layer) * kLutRows + tid;
@@ -90,53 +94,57 @@ __global__ __launch_bounds__(kLutRows) void lut_gemv_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0;
 
-  const uint32_t slices = (U + 1) >> 1;
-  for (uint32_t s = 0; s < slices; ++s) {
-    // the row's two units of the slice, requested before the tables are built
-    v4u w[2];
+  const uint32_t chunks = (U + 3) >> 2;
+  for (uint32_t c = 0; c < chunks; ++c) {
+    // the row's units of the chunk, requested before the first tables are built
+    v4u w[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t u = 2u * s + h;
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t u = 4u * c + h;
       w[h] = row_ok && u < U ? *reinterpret_cast<const v4u*>(wbase + unit_offset(n, u, N32, U)) : v4u{0, 0, 0, 0};
     }
-    // tables of the slice: thread tt builds token tt / 32, block tt % 32
-    for (int tt = tid; tt < M * kLutBlocks; tt += kLutRows) {
-      const int m = tt >> 5, g = tt & 31;
-      const uint32_t u = 2u * s + (g >> 4);
-      if (u < U) {
-        const uint32_t j = 4u * u + ((g >> 2) & 3);  // packed word of the block
-        const int b = g & 3;                          // byte of the block in that word
-        const v4u x = *reinterpret_cast<const v4u*>(Xq + m * Kp + 16 * j);
-        // bytes b, b + 4, b + 8, b + 12 of the word's 16 activations, sign-extended
-        const int sh = 8 * b;
-        const int a0 = static_cast<int>(x[0] << (24 - sh)) >> 24;
-        const int a1 = static_cast<int>(x[1] << (24 - sh)) >> 24;
-        const int a2 = static_cast<int>(x[2] << (24 - sh)) >> 24;
-        const int a3 = static_cast<int>(x[3] << (24 - sh)) >> 24;
-        build_table(tables + tt * kLutStride, a0, a1, a2, a3);
-      }
-    }
-    __syncthreads();
-    if (row_ok) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t u = 2u * s + h;
+    for (int sl = 0; sl < 4 / SU; ++sl) {
+      const uint32_t u0 = 4u * c + SU * sl;  // first unit of the slice
+      if (u0 >= U) break;
+      // tables of the slice: thread tt builds token tt / G, block tt % G
+      for (int tt = tid; tt < M * G; tt += kLutRows) {
+        const int m = tt / G, g = tt % G;
+        const uint32_t u = u0 + g / 16;
         if (u < U) {
+          const uint32_t j = 4u * u + ((g >> 2) & 3);  // packed word of the block
+          const int b = g & 3;                          // byte of the block in that word
+          const v4u x = *reinterpret_cast<const v4u*>(Xq + m * Kp + 16 * j);
+          // bytes b, b + 4, b + 8, b + 12 of the word's 16 activations, sign-extended
+          const int sh = 8 * b;
+          const int a0 = static_cast<int>(x[0] << (24 - sh)) >> 24;
+          const int a1 = static_cast<int>(x[1] << (24 - sh)) >> 24;
+          const int a2 = static_cast<int>(x[2] << (24 - sh)) >> 24;
+          const int a3 = static_cast<int>(x[3] << (24 - sh)) >> 24;
+          build_table(tables + tt * kLutStride, a0, a1, a2, a3);
+        }
+      }
+      __syncthreads();
+      if (row_ok) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t idx4 = lut_index4(w[h][q]);
+        for (int h = 0; h < SU; ++h) {
+          if (u0 + h < U) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const int g = 16 * h + 4 * q + b;
-              const uint32_t e = (idx4 >> (8 * b)) & 0xffu;
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t idx4 = lut_index4(w[SU * sl + h][q]);
 #pragma unroll
-              for (int m = 0; m < M; ++m) acc[m] += t16[(m * kLutBlocks + g) * (2 * kLutStride) + e];
+              for (int b = 0; b < 4; ++b) {
+                const int g = 16 * h + 4 * q + b;
+                const uint32_t e = (idx4 >> (8 * b)) & 0xffu;
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[m] += t16[(m * G + g) * (2 * kLutStride) + e];
+              }
             }
           }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   if (!row_ok) return;

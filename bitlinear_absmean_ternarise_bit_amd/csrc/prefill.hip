@@ -299,19 +299,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
       gload(0, S0());
     }
 
-    // epilogue: lane holds rows 8*(r/4) + 4*(l/32) + r%4, column l%32 of each 32x32 tile
+    // epilogue: lane holds rows 8*(r/4) + 4*(l/32) + r%4, column l%32 of each
+    // 32x32 tile.  The lane's first row and column are made opaque to the
+    // compiler: otherwise it hoists the per-row index arithmetic out of the
+    // tile loop, where the results stay live across the main loop and spill.
+    int lrow = wm * (BM / WM) + 4 * lh;
+    int lcol = wn * (BN / WN) + lr;
+    asm volatile("" : "+v"(lrow), "+v"(lcol));
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wm * (BM / WM) + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int row = lrow + mi * 32 + 8 * (r >> 2) + (r & 3);
         const int64_t m = em0 + row;
         if (m >= M) continue;
         const int rs = row_sum[row];
         const float scale = row_scale[row];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          const int64_t n = en0 + wn * (BN / WN) + ni * 32 + lr;
+          const int64_t n = en0 + lcol + ni * 32;
           if (n < N) {
             const int v = c[mi][ni][r] - rs;
             if constexpr (EPI == 1) acc[m * ldy + n] = v;
