@@ -7,7 +7,9 @@ namespace bitlinear {
 
 namespace {
 
-template <int DT, bool VEC>
+// RC: 16-byte chunks per lane kept in registers (rows of up to RC * 64 chunks
+// are read once)
+template <int DT, bool VEC, int RC>
 __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__ X, int64_t M, int64_t K,
                                                         int64_t Kp, int8_t* __restrict__ Xq,
                                                         float* __restrict__ gamma_a,
@@ -19,7 +21,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
   const char* row = static_cast<const char*>(X) + m * K * esize;
   float ga;
   int rs;
-  quantize_row_wave<DT, VEC>(row, K, Kp, lane, Xq + m * Kp, ga, rs);
+  quantize_row_wave<DT, VEC, RC>(row, K, Kp, lane, Xq + m * Kp, ga, rs);
   if (lane == 0) {
     gamma_a[m] = ga;
     rowsum[m] = rs;
@@ -33,10 +35,15 @@ hipError_t launch_dt(const void* X, int64_t M, int64_t K, int8_t* Xq, float* gam
   const int blocks = static_cast<int>((M + 3) / 4);
   constexpr int esize = DT == 0 ? 4 : 2;
   const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ((K * esize) % 16 == 0);
-  if (vec)
-    act_quant_kernel<DT, true><<<blocks, 256, 0, stream>>>(X, M, K, Kp, Xq, gamma_a, rowsum);
+  const int64_t chunks_per_lane = (K * esize / 16 + kWave - 1) / kWave;
+  if (!vec)
+    act_quant_kernel<DT, false, 4><<<blocks, 256, 0, stream>>>(X, M, K, Kp, Xq, gamma_a, rowsum);
+  else if (chunks_per_lane <= 4)
+    act_quant_kernel<DT, true, 4><<<blocks, 256, 0, stream>>>(X, M, K, Kp, Xq, gamma_a, rowsum);
+  else if (chunks_per_lane <= 8)
+    act_quant_kernel<DT, true, 8><<<blocks, 256, 0, stream>>>(X, M, K, Kp, Xq, gamma_a, rowsum);
   else
-    act_quant_kernel<DT, false><<<blocks, 256, 0, stream>>>(X, M, K, Kp, Xq, gamma_a, rowsum);
+    act_quant_kernel<DT, true, 16><<<blocks, 256, 0, stream>>>(X, M, K, Kp, Xq, gamma_a, rowsum);
   return hipGetLastError();
 }
 

@@ -77,26 +77,26 @@ __device__ __forceinline__ int quantize_chunk(const uint4 v, float s, int8_t* __
 
 // Quantise row `row` (K values) into dst[0..Kp) (zeros in [K, Kp)); every lane
 // of the wave must call it.  Returns gamma_A and the code sum in all lanes.
-template <int DT, bool VEC>
+// RC: a row of at most RC 16-byte chunks per lane stays in registers between
+// the two passes (one read of X instead of two).
+template <int DT, bool VEC, int RC = 4>
 __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, int64_t K, int64_t Kp,
                                                   int lane, int8_t* __restrict__ dst,
                                                   float& gamma_a, int& codesum) {
   constexpr int P = ActTraits<DT>::kPerChunk;
   if constexpr (VEC) {
-    // a row of at most four chunks per lane stays in registers between the
-    // two passes: one read of X instead of two
     const uint4* r4 = static_cast<const uint4*>(row);
     const int64_t nc = K / P;
-    if (nc <= 4 * kWave) {
-      uint4 v[4];
+    if (nc <= RC * kWave) {
+      uint4 v[RC];
       float mx = 0.0f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < RC; ++u) {
         const int64_t c = lane + u * kWave;
         v[u] = r4[c < nc ? c : nc - 1];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < RC; ++u) {
         float f[P];
         chunk_to_f32<DT>(v[u], f);
         float m = 0.0f;
@@ -108,7 +108,7 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, 
       const float s = __fdiv_rn(127.0f, __fadd_rn(mx, kEps));
       int sum = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < RC; ++u) {
         const int64_t c = lane + u * kWave;
         if (c < nc) sum += quantize_chunk<DT>(v[u], s, dst + c * P);
       }
