@@ -16,6 +16,8 @@
 //       the 2-bit format (pack_transposed_kernel) and expanded to bf16 {-1,0,1}
 //       while they are staged into LDS;
 //   dW: A = dY^T, B = A_hat^T (transposed copies, zero-padded along M).
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace bitlinear {
@@ -124,29 +126,51 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
 // (BMODE 0) or the 2-bit ternary codes of a [Q, Rp] matrix in the packed
 // format (BMODE 1), expanded to bf16 c - 1.
 // EPI 0: C * gamma;  EPI 1: C where |fp32(W[p, q] / fp32(gamma + eps))| <= 1, else 0.
-// Tile 128 x 128, 4 waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32), 64 r per
-// LDS stage, two stages; rows of an operand stage are 128 bytes with 16-byte
-// slot c of row r stored at slot c ^ (r & 7).
-template <int BMODE, int EPI>
-__global__ __launch_bounds__(256) void bf16_gemm_nt_kernel(const uint16_t* __restrict__ A, int64_t P,
-                                                           int64_t lda, const void* __restrict__ B, int64_t Q,
-                                                           int64_t Rp,
-                                                           float* __restrict__ C, int64_t ldc,
-                                                           const float* __restrict__ gamma,
-                                                           const float* __restrict__ W, int64_t ldw,
-                                                           int bytes_a, int bytes_b) {
-  constexpr int BM = 128, BN = 128, BK = 64;
+//
+// Tile BM x BN, WM x WN waves each owning (BM/WM) x (BN/WN) = 64 x (BN/WN) of
+// 32 x 32 MFMA tiles; 64 r per LDS stage, two stages.  Global loads run two
+// stages ahead into two register sets, and the next stage is written to LDS
+// halfway through the contraction of the current one, so one barrier per
+// stage suffices and the matrix cores keep working while loads are in flight.
+// Operand rows of a stage are 128 bytes with 16-byte slot c of row r stored at
+// slot c ^ ((r >> 1) & 7): the 16 lanes one LDS cycle serves (16 consecutive
+// rows, same slot) hit distinct bank groups of the 64-bank LDS.
+template <int BM, int BN, int WM, int WN, int BMODE, int EPI>
+__global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
+    const uint16_t* __restrict__ A, int64_t P, int64_t lda, const void* __restrict__ B, int64_t Q, int64_t Rp,
+    float* __restrict__ C, int64_t ldc, const float* __restrict__ gamma, const float* __restrict__ W,
+    int64_t ldw, int bytes_a, int bytes_b, int tiles_p, int tiles_q) {
+  constexpr int BK = 64;
   constexpr int ROWB = BK * 2;
+  constexpr int THREADS = 64 * WM * WN;
   constexpr int A_BYTES = BM * ROWB;
   constexpr int STAGE = A_BYTES + BN * ROWB;
-  __shared__ __align__(16) char smem[2 * STAGE];
+  constexpr int MI = BM / WM / 32, NI = BN / WN / 32;
+  constexpr int A_LOADS = BM * 8 / THREADS;
+  constexpr int B_LOADS = BMODE == 0 ? BN * 8 / THREADS : 1;
+  static_assert(BM / WM == 64 && A_LOADS >= 1 && B_LOADS >= 1 && NI >= 1, "tile shape");
+  static_assert(BMODE == 0 || BN <= THREADS, "one packed row per thread");
+  __shared__ __align__(1024) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t p0 = static_cast<int64_t>(blockIdx.y) * BM;
-  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * BN;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // Workgroup -> tile: each XCD (workgroups are dealt round-robin to the 8
+  // XCDs) gets a contiguous run of tiles, walked in groups of 8 tile rows so
+  // resident tiles share operand panels in the XCD's L2.
+  const int num_tiles = tiles_p * tiles_q;
+  int t = blockIdx.x;
+  if (num_tiles % 8 == 0) t = (t & 7) * (num_tiles >> 3) + (t >> 3);
+  constexpr int GROUP = 8;
+  const int group = t / (GROUP * tiles_q);
+  const int first_p = group * GROUP;
+  const int gsize = min(tiles_p - first_p, GROUP);
+  const int in_group = t - group * GROUP * tiles_q;
+  const int64_t p0 = static_cast<int64_t>(first_p + in_group % gsize) * BM;
+  const int64_t q0 = static_cast<int64_t>(in_group / gsize) * BN;
+
   const int niter = static_cast<int>(Rp / BK);
   const uint32_t rowbytes = static_cast<uint32_t>(Rp) * 2u;
   const uint32_t rowbytes_a = static_cast<uint32_t>(lda) * 2u;
@@ -157,50 +181,61 @@ __global__ __launch_bounds__(256) void bf16_gemm_nt_kernel(const uint16_t* __res
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(B), 0, bytes_b, 0x00020000);
   constexpr uint32_t kOff = 0x80000000u;  // past every resource: reads zeros
 
-  // A (and dense B): 128 rows x 8 slots per stage, 4 slots per thread
-  uint32_t a_off[4], a_dst[4], b_off[4];
+  // operand slot s = tid + THREADS i: row s / 8, logical slot s % 8
+  uint32_t a_off[A_LOADS], a_dst[A_LOADS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = tid + 256 * i, r = s >> 3, c = s & 7;
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int s = tid + THREADS * i, r = s >> 3, c = s & 7;
     a_off[i] = (p0 + r < P) ? static_cast<uint32_t>(p0 + r) * rowbytes_a + 16u * c : kOff;
-    b_off[i] = (q0 + r < Q) ? static_cast<uint32_t>(q0 + r) * rowbytes + 16u * c : kOff;
-    a_dst[i] = r * ROWB + 16 * (c ^ (r & 7));
+    a_dst[i] = r * ROWB + 16 * (c ^ ((r >> 1) & 7));
   }
-  // packed B: thread tid < 128 stages row tid (one 16-byte unit of 64 codes)
+  uint32_t b_off[B_LOADS], b_dst[B_LOADS];
+  if constexpr (BMODE == 0) {
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int s = tid + THREADS * i, r = s >> 3, c = s & 7;
+      b_off[i] = (q0 + r < Q) ? static_cast<uint32_t>(q0 + r) * rowbytes + 16u * c : kOff;
+      b_dst[i] = A_BYTES + r * ROWB + 16 * (c ^ ((r >> 1) & 7));
+    }
+  }
+  // packed B: thread tid < BN stages row tid (one 16-byte unit of 64 codes)
   const uint32_t units = static_cast<uint32_t>(Rp >> 6);
   const bool pb_row = tid < BN && q0 + tid < Q;
 
-  v4u ra[4], rb[4];
-  auto gload = [&](int it) {
+  v4u ra[2][A_LOADS], rb[2][B_LOADS];
+  auto gload = [&](int it, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[i] == kOff ? kOff : a_off[i] + 128u * it, 0, 0);
+    for (int i = 0; i < A_LOADS; ++i)
+      ra[S][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[i] == kOff ? kOff : a_off[i] + 128u * it, 0, 0);
     if constexpr (BMODE == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, b_off[i] == kOff ? kOff : b_off[i] + 128u * it, 0, 0);
+      for (int i = 0; i < B_LOADS; ++i)
+        rb[S][i] =
+            __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, b_off[i] == kOff ? kOff : b_off[i] + 128u * it, 0, 0);
     } else {
       const uint32_t off = pb_row ? unit_offset(static_cast<uint32_t>(q0 + tid), static_cast<uint32_t>(it),
                                                 static_cast<uint32_t>(Q), units)
                                   : kOff;
-      rb[0] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, off, 0, 0);
+      if (tid < BN) rb[S][0] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, off, 0, 0);
     }
   };
-  auto swrite = [&](char* st) {
+  auto swrite = [&](char* st, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(st + a_dst[i]) = ra[i];
-    char* sb = st + A_BYTES;
+    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<v4u*>(st + a_dst[i]) = ra[S][i];
     if constexpr (BMODE == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(sb + a_dst[i]) = rb[i];
+      for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<v4u*>(st + b_dst[i]) = rb[S][i];
     } else if (tid < BN) {
       // 64 codes -> 64 bf16 values c - 1 through two byte tables (v_perm):
       // high bytes {0xBF, 0x00, 0x3F} and low bytes {0x80, 0x00, 0x80} for c = 0, 1, 2
       constexpr uint32_t kHi = 0x003F00BFu, kLo = 0x00800080u;
       const int r = tid;
+      char* sb = st + A_BYTES + r * ROWB;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {  // slot c: k = 8c .. 8c + 7 = word c/2, fields i = 2(c%2), 2(c%2)+1
-        const uint32_t w = rb[0][c >> 1];
+        const uint32_t w = rb[S][0][c >> 1];
         v4u out;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -210,72 +245,154 @@ __global__ __launch_bounds__(256) void bf16_gemm_nt_kernel(const uint16_t* __res
           out[2 * h] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
           out[2 * h + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
         }
-        *reinterpret_cast<v4u*>(sb + r * ROWB + 16 * (c ^ (r & 7))) = out;
+        *reinterpret_cast<v4u*>(sb + 16 * (c ^ ((r >> 1) & 7))) = out;
       }
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MI][NI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int lr = lane & 31, lh = lane >> 5;
-  gload(0);
-  swrite(smem);
-  __syncthreads();
-  for (int it = 0; it < niter; ++it) {
-    char* cur = smem + (it & 1) * STAGE;
-    gload(it + 1 < niter ? it + 1 : it);
+  // LDS byte offsets of this lane's operands for k step ks of a stage (slot
+  // 2 ks + lh of its row); tile mi / ni adds 32 rows = 4096 bytes
+  int a_rd[4], b_rd[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int slot = 2 * ks + lh;
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + lr;
-        a[i] = *reinterpret_cast<const bf16x8*>(cur + r * ROWB + 16 * (slot ^ (r & 7)));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + lr;
-        b[j] = *reinterpret_cast<const bf16x8*>(cur + A_BYTES + r * ROWB + 16 * (slot ^ (r & 7)));
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    swrite(smem + ((it + 1) & 1) * STAGE);
-    __syncthreads();
+  for (int ks = 0; ks < 4; ++ks) {
+    const int sw = 16 * ((2 * ks + lh) ^ ((lr >> 1) & 7));
+    a_rd[ks] = (wm * 64 + lr) * ROWB + sw;
+    b_rd[ks] = A_BYTES + (wn * (BN / WN) + lr) * ROWB + sw;
   }
+  auto contract_half = [&](const char* st, int hs) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ks = 2 * hs + kk;
+      bf16x8 a[MI], b[NI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) a[i] = *reinterpret_cast<const bf16x8*>(st + a_rd[ks] + i * 32 * ROWB);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) b[j] = *reinterpret_cast<const bf16x8*>(st + b_rd[ks] + j * 32 * ROWB);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
 
-  // epilogue: lane holds rows 8 (e / 4) + 4 lh + e % 4, column lr of each 32 x 32 tile
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // prologue: stage 0 -> LDS 0; stage 1 in register set 1; stage 2 loading into set 0
+  gload(0, S0());
+  gload(min(1, niter - 1), S1());
+  swrite(smem, S0());
+  gload(min(2, niter - 1), S0());
+  __syncthreads();
+
+  // Iteration it contracts LDS stage it % 2; halfway it writes stage it + 1
+  // (register set (it + 1) % 2, loaded two iterations earlier) into the other
+  // LDS stage and reloads that register set with stage it + 3 (past the last
+  // stage: the last stage again, written to the idle LDS stage, harmless).
+  auto iteration = [&](int it, auto set_tag) {
+    const char* cur = smem + (it & 1) * STAGE;
+    char* nxt = smem + ((it + 1) & 1) * STAGE;
+    contract_half(cur, 0);
+    swrite(nxt, set_tag);
+    gload(min(it + 3, niter - 1), set_tag);
+    contract_half(cur, 1);
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it + 1 < niter; it += 2) {
+    iteration(it, S1());
+    iteration(it + 1, S0());
+  }
+  if (it < niter) iteration(it, S1());
+
+  // epilogue: lane holds rows 8 (e / 4) + 4 lh + e % 4, column lr of each
+  // 32 x 32 tile.  The lane's first row and column are opaque to the
+  // compiler, so it does not compute the output addresses before the main
+  // loop and keep them live (spilled) across it.
+  int lrow = wm * 64 + 4 * lh;
+  int lcol = wn * (BN / WN) + lr;
+  asm volatile("" : "+v"(lrow), "+v"(lcol));
   const float g = gamma[0];
   const float d = __fadd_rn(g, kEps);
+  if constexpr (EPI == 0) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t p = p0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-      if (p >= P) continue;
+      for (int e = 0; e < 16; ++e) {
+        const int64_t p = p0 + lrow + i * 32 + 8 * (e >> 2) + (e & 3);
+        if (p >= P) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t q = q0 + wn * 64 + j * 32 + lr;
-        if (q >= Q) continue;
-        float v = acc[i][j][e];
-        if constexpr (EPI == 0) {
-          v = __fmul_rn(v, g);
-        } else {
-          const float t = __fdiv_rn(W[p * ldw + q], d);
-          v = fabsf(t) <= 1.0f ? v : 0.0f;
+        for (int j = 0; j < NI; ++j) {
+          const int64_t q = q0 + lcol + j * 32;
+          if (q < Q) C[p * ldc + q] = __fmul_rn(acc[i][j][e], g);
         }
-        C[p * ldc + q] = v;
       }
+  } else {
+    // The range mask of the tile goes into LDS first, one bit per output:
+    // vector-memory operations complete in order, so W loads interleaved
+    // with the output stores would each wait for the stores before them.
+    // Wave w reads W for tile rows [32 w, 32 w + 32), lane l holding columns
+    // 64 k + l; a ballot per (row, k) is that row's 64-column bit word.
+    constexpr int WPR = BN / 64;          // 64-bit words per tile row
+    constexpr int RPW = BM / (WM * WN);   // tile rows per wave
+    uint64_t* mbits = reinterpret_cast<uint64_t*>(smem);  // [BM][WPR]; every wave is past the last stage
+#pragma unroll 1
+    for (int r0 = wave * RPW; r0 < (wave + 1) * RPW; r0 += 4) {
+      float wv[4][WPR];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int64_t p = p0 + r0 + rr;
+#pragma unroll
+        for (int k = 0; k < WPR; ++k) {
+          const int64_t q = q0 + 64 * k + lane;
+          wv[rr][k] = (p < P && q < Q) ? W[p * ldw + q] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int k = 0; k < WPR; ++k) {
+          const uint64_t bits = __ballot(fabsf(__fdiv_rn(wv[rr][k], d)) <= 1.0f);
+          if (lane == 0) mbits[(r0 + rr) * WPR + k] = bits;
+        }
     }
+    __syncthreads();
+    const uint32_t* mb32 = reinterpret_cast<const uint32_t*>(smem);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = lrow + i * 32 + 8 * (e >> 2) + (e & 3);
+        const int64_t p = p0 + row;
+        if (p >= P) continue;
+        // bit lr of words (row, column block lcol / 32 + j): columns lcol + 32 j
+        const uint32_t* wrow = mb32 + row * (2 * WPR) + (lcol >> 5);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int64_t q = q0 + lcol + j * 32;
+          if (q >= Q) continue;
+          C[p * ldc + q] = (wrow[j] >> lr) & 1u ? acc[i][j][e] : 0.0f;
+        }
+      }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int BMODE, int EPI>
+void launch_gemm(const uint16_t* A, int64_t P, int64_t lda, const void* B, int64_t Q, int64_t Rp, float* C,
+                 int64_t ldc, const float* gamma, const float* W, int64_t ldw, int bytes_a, int bytes_b,
+                 hipStream_t stream) {
+  const int tiles_p = static_cast<int>((P + BM - 1) / BM), tiles_q = static_cast<int>((Q + BN - 1) / BN);
+  bf16_gemm_nt_kernel<BM, BN, WM, WN, BMODE, EPI><<<static_cast<unsigned>(tiles_p * tiles_q), 64 * WM * WN, 0,
+                                                    stream>>>(A, P, lda, B, Q, Rp, C, ldc, gamma, W, ldw, bytes_a,
+                                                              bytes_b, tiles_p, tiles_q);
 }
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -313,21 +430,18 @@ hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, 
       if (blocks > 65536) blocks = 65536;
       pad_rows_bf16_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(dY, M, N, dYp, Np);
     }
-    const dim3 grid(static_cast<unsigned>((K + 127) / 128), static_cast<unsigned>((M + 127) / 128));
-    bf16_gemm_nt_kernel<1, 0><<<grid, 256, 0, stream>>>(direct ? dY : dYp, M, direct ? N : Np, packedT, K, Np,
-                                                         dX, K, gamma, nullptr, 0,
-                                                         static_cast<int>(M * (direct ? N : Np) * 2),
-                                                         static_cast<int>(K * (Np / 4)));
+    // 256 x 128 tiles: a 2048-token, 4096-column dX is 256 tiles, one per CU
+    launch_gemm<256, 128, 4, 2, 1, 0>(direct ? dY : dYp, M, direct ? N : Np, packedT, K, Np, dX, K, gamma,
+                                      nullptr, 0, static_cast<int>(M * (direct ? N : Np) * 2),
+                                      static_cast<int>(K * (Np / 4)), stream);
   }
   if (dW) {
     const dim3 g0(static_cast<unsigned>((N + kTile - 1) / kTile), static_cast<unsigned>(Mp / kTile));
     transpose_kernel<0><<<g0, 256, 0, stream>>>(dY, M, N, N, nullptr, dYt, Mp);
     const dim3 g1(static_cast<unsigned>((K + kTile - 1) / kTile), static_cast<unsigned>(Mp / kTile));
     transpose_kernel<1><<<g1, 256, 0, stream>>>(Xq, M, K, Kp, gamma_a, At, Mp);
-    const dim3 grid(static_cast<unsigned>((K + 127) / 128), static_cast<unsigned>((N + 127) / 128));
-    bf16_gemm_nt_kernel<0, 1><<<grid, 256, 0, stream>>>(dYt, N, Mp, At, K, Mp, dW, K, gamma, W, K,
-                                                         static_cast<int>(N * Mp * 2),
-                                                         static_cast<int>(K * Mp * 2));
+    launch_gemm<256, 256, 4, 2, 0, 1>(dYt, N, Mp, At, K, Mp, dW, K, gamma, W, K, static_cast<int>(N * Mp * 2),
+                                      static_cast<int>(K * Mp * 2), stream);
   }
   return hipGetLastError();
 }
