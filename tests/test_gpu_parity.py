@@ -167,6 +167,33 @@ FORWARD_CASES = [
 ]
 
 
+# Persistent prefill workgroups (one per CU) walking several tiles each: tile
+# counts above 256, with and without the XCD remap (count % 8), one-stage and
+# half-stage K, ragged M and N.
+PERSISTENT_CASES = [
+    (4100, 1050, 5000, "bf16"),  # 340 tiles (no remap), half K stage, ragged M and N
+    (4096, 640, 5120, "f32"),    # 320 tiles (remapped), five stages
+    (4096, 100, 5120, "bf16"),   # one stage per tile
+    (4096, 64, 5120, "f32"),     # a single half stage per tile
+]
+
+
+@pytest.mark.parametrize("M,K,N,dt", PERSISTENT_CASES)
+def test_prefill_persistent_tiles(M, K, N, dt):
+    say(f"prefill persistent M={M} K={K} N={N} {dt}")
+    P = random_problem(M, K, N, seed=M + 3 * K + 5 * N, x_dtype=dt)
+    W = torch.from_numpy(P.W).to(DEV)
+    X = dev_x(P)
+    packed, gamma = bl.quantize_weights(W)
+    Y, acc = bl.forward(X, packed, gamma, K, path="prefill", return_acc=True)
+    Y_only = bl.forward(X, packed, gamma, K, path="prefill")
+    torch.cuda.synchronize()
+    ref = O.bitlinear_forward(P.X, P.W)
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    check_y(Y.cpu().numpy(), ref["Y"])
+    assert torch.equal(Y, Y_only)  # the Y-only epilogue equals the one that also stores acc
+
+
 @pytest.mark.parametrize("M,K,N,dt,path", FORWARD_CASES)
 def test_forward_parity(M, K, N, dt, path):
     say(f"forward M={M} K={K} N={N} {dt} {path}")
