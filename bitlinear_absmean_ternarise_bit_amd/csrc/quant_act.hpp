@@ -75,6 +75,28 @@ __device__ __forceinline__ int quantize_chunk(const uint4 v, float s, int8_t* __
   return sum;
 }
 
+// Codes of row `row` (K values) with scale s into dst[0..Kp) (zeros in
+// [K, Kp)), one pass; returns this lane's part of the code sum.
+template <int DT, bool VEC>
+__device__ __forceinline__ int codes_pass(const void* __restrict__ row, int64_t K, int64_t Kp, int lane,
+                                          int8_t* __restrict__ dst, float s) {
+  constexpr int P = ActTraits<DT>::kPerChunk;
+  int sum = 0;
+  if constexpr (VEC) {
+    const uint4* r4 = static_cast<const uint4*>(row);
+    const int64_t nc = K / P;
+    for (int64_t c = lane; c < nc; c += kWave) sum += quantize_chunk<DT>(r4[c], s, dst + c * P);
+  } else {
+    for (int64_t k = lane; k < K; k += kWave) {
+      const int code = act_code(load_one<DT>(row, k), s);
+      sum += code;
+      dst[k] = static_cast<int8_t>(code);
+    }
+  }
+  for (int64_t k = K + lane; k < Kp; k += kWave) dst[k] = 0;
+  return sum;
+}
+
 // Quantise row `row` (K values) into dst[0..Kp) (zeros in [K, Kp)); every lane
 // of the wave must call it.  Returns gamma_A and the code sum in all lanes.
 // RC: a row of at most RC 16-byte chunks per lane stays in registers between
@@ -147,21 +169,8 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, 
   mx = wave_max(mx);
   const float s = __fdiv_rn(127.0f, __fadd_rn(mx, kEps));
 
-  int sum = 0;
-  if constexpr (VEC) {
-    const uint4* r4 = static_cast<const uint4*>(row);
-    const int64_t nc = K / P;
-    for (int64_t c = lane; c < nc; c += kWave) sum += quantize_chunk<DT>(r4[c], s, dst + c * P);
-  } else {
-    for (int64_t k = lane; k < K; k += kWave) {
-      const int code = act_code(load_one<DT>(row, k), s);
-      sum += code;
-      dst[k] = static_cast<int8_t>(code);
-    }
-  }
-  for (int64_t k = K + lane; k < Kp; k += kWave) dst[k] = 0;
   gamma_a = mx;
-  codesum = wave_sum(sum);
+  codesum = wave_sum(codes_pass<DT, VEC>(row, K, Kp, lane, dst, s));
 }
 
 }  // namespace bitlinear

@@ -111,7 +111,8 @@ def test_gamma_independent_of_grid_scheduling():
 
 @pytest.mark.parametrize("M,K,dt", [(1, 1, "f32"), (5, 100, "bf16"), (7, 64, "f32"), (33, 2048, "bf16"),
                                     (6, 4096, "bf16"), (3, 2048, "f32"), (5, 4096, "f32"), (2, 8192, "f32"),
-                                    (3, 4104, "bf16"), (2, 16384, "bf16"),
+                                    (3, 4104, "bf16"), (2, 16384, "bf16"), (3, 11008, "f32"),
+                                    (2, 16384, "f32"), (1, 20000, "f32"), (2, 33000, "bf16"),
                                     (4, 8191, "f32"), (9, 8192, "bf16"), (130, 136, "bf16")])
 def test_quantize_activations_bit_exact(M, K, dt):
     say(f"quantize_activations M={M} K={K} {dt}")
