@@ -11,7 +11,7 @@ from .bitlinear_oracle import (EPS32, absmax_quantize, absmean_gamma, absmean_ga
                                zero_gemm_dot, zero_gemm_naive)
 from .bitlinear_oracle import deinterleave_units, interleave_units
 from .bitlinear_oracle import dequant_f32, ffn_forward, ffn_from_codes, relu2
-from .bitlinear_oracle import dequant_activations_bf16, ste_backward, ste_weight_mask
+from .bitlinear_oracle import dequant_activations_bf16, pack_mask_bits, ste_backward, ste_weight_mask, unpack_mask_bits
 from .bitlinear_oracle import (R3_UNIT, pack_codes_r3, r3_byte, r3_packed_bytes, r3_padded_k,
                                r3_value, r3_value_of_byte, unpack_codes_r3)
 from .bitlinear_oracle import (LUT_ENTRIES, LUT_GROUP, lut_digits, lut_forward, lut_gemv, lut_index,

@@ -548,6 +548,29 @@ def ste_weight_mask(W: np.ndarray, gamma) -> np.ndarray:
     return (np.abs(t) <= np.float32(1.0))
 
 
+def pack_mask_bits(mask: np.ndarray) -> np.ndarray:
+    """The range mask [N, K] as bits: uint32 [N, ceil(K / 32)], bit k % 32 of
+    word k // 32 of row n is mask[n, k]; bits past K are 0.  (A storage format
+    of this library: the mask depends only on W and gamma, so it is formed
+    once per weight update next to the transposed codes.)"""
+    mask = np.asarray(mask, dtype=bool)
+    N, K = mask.shape
+    Kw = -(-K // 32)
+    bits = np.zeros((N, Kw * 32), dtype=np.uint64)
+    bits[:, :K] = mask
+    shifts = np.arange(32, dtype=np.uint64)
+    words = (bits.reshape(N, Kw, 32) << shifts).sum(axis=2)
+    return words.astype(np.uint32)
+
+
+def unpack_mask_bits(words: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of pack_mask_bits: bool [N, K]."""
+    words = np.asarray(words, dtype=np.uint32)
+    N, Kw = words.shape
+    bits = (words[:, :, None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1)
+    return bits.reshape(N, Kw * 32)[:, :K].astype(bool)
+
+
 def ste_backward(dY: np.ndarray, q: np.ndarray, gamma, Xq: np.ndarray, gamma_a: np.ndarray,
                  W: np.ndarray) -> Dict[str, np.ndarray]:
     """dX [M, K] and dW [N, K] (float32) of the forward Y = A_hat W_hat^T under the STE.

@@ -98,3 +98,25 @@ def test_loops_on_a_tiny_problem():
         for k in range(K):
             s = sum(float(dY[m, n]) * float(A[m, k]) for m in range(M))
             assert ref["dW"][n, k] == (np.float32(s) if mask[n, k] else 0.0)
+
+
+def test_mask_bits_hand_worked():
+    # row 0: k = 0, 3, 31 in range -> bits 0, 3, 31 of word 0 = 0x80000009;
+    # k = 32 in range -> bit 0 of word 1 = 0x1 (K = 33: bits past K stay 0)
+    mask = np.zeros((2, 33), dtype=bool)
+    mask[0, [0, 3, 31, 32]] = True
+    mask[1, 1] = True
+    words = O.pack_mask_bits(mask)
+    assert words.dtype == np.uint32 and words.shape == (2, 2)
+    assert words.tolist() == [[0x80000009, 0x1], [0x2, 0x0]]
+
+
+def test_mask_bits_round_trip():
+    rng = np.random.default_rng(9)
+    for K in (1, 31, 32, 33, 64, 1000):
+        mask = rng.random((7, K)) < 0.7
+        words = O.pack_mask_bits(mask)
+        assert words.shape == (7, -(-K // 32))
+        assert np.array_equal(O.unpack_mask_bits(words, K), mask)
+        if K % 32:
+            assert not np.any(words[:, -1] >> np.uint32(K % 32))  # bits past K are 0
