@@ -516,12 +516,14 @@ def bench_backward(args, torch, bl, dev):
     g.manual_seed(1234)
     dY = torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16)
     packedT = torch.empty((K, bl.packed_words(N)), dtype=torch.int32, device=dev)
+    mask = torch.empty((N, (K + 31) // 32), dtype=torch.int32, device=dev)
+    bl.pack_transposed(W, gamma, out=packedT, mask_out=mask)  # warm
     with Timer(torch) as tp:
-        bl.pack_transposed(W, gamma, out=packedT)
+        bl.pack_transposed(W, gamma, out=packedT, mask_out=mask)
     ws = torch.empty((bl.abi.load().bitlinear_backward_workspace_bytes(M, N, K),), dtype=torch.uint8, device=dev)
 
     def step():
-        bl.backward(dY, packedT, gamma, Xq, ga, W, workspace=ws)
+        bl.backward(dY, packedT, gamma, Xq, ga, mask, K, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -541,7 +543,8 @@ def bench_backward(args, torch, bl, dev):
            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
                         "kernel": "bf16_gemm_nt_kernel x 2 + operand preparation, one step"},
-           "pack_transposed": {"ms": round(tp.ms, 4), "note": "codes of W^T, once per weight update"}}
+           "pack_transposed": {"ms": round(tp.ms, 4),
+                               "note": "codes of W^T and the range mask of W, once per weight update"}}
     if args.cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_backward(P, args.cpu_seconds)
     return out

@@ -409,32 +409,36 @@ def ffn_forward(X, up, down, path: str = "auto", return_hidden: bool = False, ou
 
 # ---- backward with the straight-through estimator ---------------------------
 
-def pack_transposed(W, gamma, out=None):
-    """Codes of W^T ([K, padded_k(N) // 16] words) for the backward's dX; gamma from quantize_weights(W)."""
+def pack_transposed(W, gamma, out=None, mask_out=None):
+    """What the backward needs from W (once per weight update): the codes of
+    W^T ([K, padded_k(N) // 16] words, for dX) and the range mask (int32
+    [N, ceil(K / 32)] bit words, for dW); gamma from quantize_weights(W)."""
     torch = _torch()
     _require_cuda(W, "W")
     _require_cuda(gamma, "gamma")
     N, K = W.shape
     lib = abi.load()
     packedT = out if out is not None else torch.empty((K, packed_words(N)), dtype=torch.int32, device=W.device)
+    mask = mask_out if mask_out is not None else torch.empty((N, (K + 31) // 32), dtype=torch.int32,
+                                                             device=W.device)
     abi.check("bitlinear_pack_transposed",
-              lib.bitlinear_pack_transposed(_ptr(W), N, K, _ptr(gamma), _ptr(packedT), _stream(W)))
-    return packedT
+              lib.bitlinear_pack_transposed(_ptr(W), N, K, _ptr(gamma), _ptr(packedT), _ptr(mask), _stream(W)))
+    return packedT, mask
 
 
-def backward(dY, packedT, gamma, Xq, gamma_a, W, need_dx: bool = True, need_dw: bool = True, workspace=None):
+def backward(dY, packedT, gamma, Xq, gamma_a, mask, K: int, need_dx: bool = True, need_dw: bool = True,
+             workspace=None):
     """STE gradients (dX [M, K], dW [N, K], float32) of the forward from dY (bfloat16 [M, N]).
 
     ``Xq``/``gamma_a``: the forward's activation codes (quantize_activations);
-    ``W``: float32 [N, K] weights; ``packedT``: pack_transposed(W, gamma).
+    ``packedT``/``mask``: pack_transposed(W, gamma); K: the weights' columns.
     """
     torch = _torch()
-    for t, nm in ((dY, "dY"), (gamma, "gamma"), (W, "W")):
+    for t, nm in ((dY, "dY"), (gamma, "gamma")):
         _require_cuda(t, nm)
     if dY.dtype != torch.bfloat16:
         raise ValueError("dY must be bfloat16")
     M, N = dY.shape
-    K = W.shape[1]
     lib = abi.load()
     dX = torch.empty((M, K), dtype=torch.float32, device=dY.device) if need_dx else None
     dW = torch.empty((N, K), dtype=torch.float32, device=dY.device) if need_dw else None
@@ -443,6 +447,6 @@ def backward(dY, packedT, gamma, Xq, gamma_a, W, need_dx: bool = True, need_dw: 
                                 device=dY.device)
     abi.check("bitlinear_backward",
               lib.bitlinear_backward(_ptr(dY), M, N, K, _ptr(packedT), _ptr(gamma), _ptr(Xq), _ptr(gamma_a),
-                                     _ptr(W), _ptr(dX), _ptr(dW), _ptr(workspace),
+                                     _ptr(mask), _ptr(dX), _ptr(dW), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(dY)))
     return dX, dW

@@ -47,7 +47,8 @@ SIGNATURES = {
     "bitlinear_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "bitlinear_ffn_forward": (_int, [_i64, _p, _int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int,
                                      _p, _sz, _p]),
-    "bitlinear_pack_transposed": (_int, [_p, _i64, _i64, _p, _p, _p]),
+    "bitlinear_ste_mask_bytes": (_sz, [_i64, _i64]),
+    "bitlinear_pack_transposed": (_int, [_p, _i64, _i64, _p, _p, _p, _p]),
     "bitlinear_backward_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bitlinear_backward": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "bitlinear_r3_padded_k": (_i64, [_i64]),

@@ -243,15 +243,21 @@ int bitlinear_ffn_forward(int64_t L, const void* X, int x_dtype, int64_t M, int6
   return BITLINEAR_OK;
 }
 
+size_t bitlinear_ste_mask_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(mask_words(K)) * 4;
+}
+
 int bitlinear_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma, uint32_t* packedT,
-                              void* stream) {
-  if (!W || !gamma || !packedT) return BITLINEAR_ERR_NULL;
+                              uint32_t* mask, void* stream) {
+  if (!W || !gamma || (!packedT && !mask)) return BITLINEAR_ERR_NULL;
   int st = check_mnk(1, N, K);
   if (st) return st;
   st = check_mnk(1, K, N);
   if (st) return st;
-  if (!aligned(W, 4) || !aligned(gamma, 4) || !aligned(packedT, 16)) return BITLINEAR_ERR_ALIGN;
-  return hip_status(launch_pack_transposed(W, N, K, gamma, packedT, static_cast<hipStream_t>(stream)));
+  if (!aligned(W, 4) || !aligned(gamma, 4) || (packedT && !aligned(packedT, 16)) || (mask && !aligned(mask, 4)))
+    return BITLINEAR_ERR_ALIGN;
+  return hip_status(launch_pack_transposed(W, N, K, gamma, packedT, mask, static_cast<hipStream_t>(stream)));
 }
 
 size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -260,11 +266,11 @@ size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 int bitlinear_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, const uint32_t* packedT,
-                       const float* gamma, const int8_t* Xq, const float* gamma_a, const float* W, float* dX,
-                       float* dW, void* workspace, size_t workspace_bytes, void* stream) {
+                       const float* gamma, const int8_t* Xq, const float* gamma_a, const uint32_t* mask,
+                       float* dX, float* dW, void* workspace, size_t workspace_bytes, void* stream) {
   if (!dY || !gamma || (!dX && !dW)) return BITLINEAR_ERR_NULL;
   if (dX && !packedT) return BITLINEAR_ERR_NULL;
-  if (dW && (!Xq || !gamma_a || !W)) return BITLINEAR_ERR_NULL;
+  if (dW && (!Xq || !gamma_a || !mask)) return BITLINEAR_ERR_NULL;
   int st = check_mnk(M, N, K);
   if (st) return st;
   st = check_mnk(M, K, N);
@@ -274,12 +280,12 @@ int bitlinear_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, cons
   const int64_t lim = int64_t(1) << 31;
   if (M * padded_k(N) * 2 >= lim || N * Mp * 2 >= lim || K * Mp * 2 >= lim) return BITLINEAR_ERR_SHAPE;
   if (!aligned(dY, 2) || !aligned(gamma, 4) || (packedT && !aligned(packedT, 16)) ||
-      (gamma_a && !aligned(gamma_a, 4)) || (W && !aligned(W, 4)) || (dX && !aligned(dX, 4)) ||
+      (gamma_a && !aligned(gamma_a, 4)) || (mask && !aligned(mask, 4)) || (dX && !aligned(dX, 4)) ||
       (dW && !aligned(dW, 4)))
     return BITLINEAR_ERR_ALIGN;
   if (!workspace || workspace_bytes < backward_workspace_bytes(M, N, K)) return BITLINEAR_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return BITLINEAR_ERR_ALIGN;
-  return hip_status(launch_backward(dY, M, N, K, packedT, gamma, Xq, gamma_a, W, dX, dW, workspace,
+  return hip_status(launch_backward(dY, M, N, K, packedT, gamma, Xq, gamma_a, mask, dX, dW, workspace,
                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -42,24 +42,37 @@ __device__ __forceinline__ uint32_t offset_code(float w, float d, bool valid) {
 }
 
 // Codes of W^T ([K rows of Np = padded_k(N) codes]) in the 2-bit format and
-// its interleaved row order.  One workgroup per 64 (n) x 64 (k) tile of W:
+// its interleaved row order, and the range mask of W as bits (bit k % 32 of
+// word k / 32 of row n: |fp32(W[n, k] / fp32(gamma + eps))| <= 1; bits past K
+// are 0; words per row Kw).  One workgroup per 64 (n) x 64 (k) tile of W:
 // codes go through LDS transposed, then each thread writes one word (16
-// consecutive n of one k).
+// consecutive n of one k); a wave reads 64 consecutive k of one row, so one
+// ballot is that row's two mask words.  Either output may be NULL.
 __global__ __launch_bounds__(256) void pack_transposed_kernel(const float* __restrict__ W, int64_t N,
                                                               int64_t K, const float* __restrict__ gamma,
-                                                              uint32_t* __restrict__ packedT, int64_t Np) {
+                                                              uint32_t* __restrict__ packedT, int64_t Np,
+                                                              uint32_t* __restrict__ mask, int64_t Kw) {
   __shared__ uint8_t codes[kTile][kTile + 4];  // [k][n]
   const float d = __fadd_rn(gamma[0], kEps);
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTile;
   const int64_t k0 = static_cast<int64_t>(blockIdx.y) * kTile;
   const int tid = threadIdx.x;
   for (int idx = tid; idx < kTile * kTile; idx += 256) {
-    const int nl = idx >> 6, kl = idx & 63;  // consecutive threads: consecutive k of one row n
+    const int nl = idx >> 6, kl = idx & 63;  // a wave: k0 .. k0 + 63 of one row n
     const int64_t n = n0 + nl, k = k0 + kl;
     const bool valid = n < N && k < K;
     const float w = valid ? W[n * K + k] : 0.0f;
     codes[kl][nl] = static_cast<uint8_t>(offset_code(w, d, n < N));
+    if (mask) {
+      const uint64_t bits = __ballot(valid && fabsf(__fdiv_rn(w, d)) <= 1.0f);
+      if ((tid & 63) == 0 && n < N) {
+        const int64_t wd = k0 >> 5;
+        mask[n * Kw + wd] = static_cast<uint32_t>(bits);
+        if (wd + 1 < Kw) mask[n * Kw + wd + 1] = static_cast<uint32_t>(bits >> 32);
+      }
+    }
   }
+  if (!packedT) return;
   __syncthreads();
   const int kl = tid >> 2, jw = tid & 3;
   const int64_t k = k0 + kl;
@@ -125,7 +138,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
 // past a row's end only meets zeros); rows 16-byte aligned.  B: bf16 [Q, Rp]
 // (BMODE 0) or the 2-bit ternary codes of a [Q, Rp] matrix in the packed
 // format (BMODE 1), expanded to bf16 c - 1.
-// EPI 0: C * gamma;  EPI 1: C where |fp32(W[p, q] / fp32(gamma + eps))| <= 1, else 0.
+// EPI 0: C * gamma;  EPI 1: C where bit q of row p of the range mask is set
+// (mask: rows of kw 32-bit words, bit q % 32 of word q / 32), else 0.
 //
 // Tile BM x BN, WM x WN waves each owning (BM/WM) x (BN/WN) = 64 x (BN/WN) of
 // 32 x 32 MFMA tiles; 64 r per LDS stage, two stages.  Global loads run two
@@ -138,8 +152,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
 template <int BM, int BN, int WM, int WN, int BMODE, int EPI>
 __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
     const uint16_t* __restrict__ A, int64_t P, int64_t lda, const void* __restrict__ B, int64_t Q, int64_t Rp,
-    float* __restrict__ C, int64_t ldc, const float* __restrict__ gamma, const float* __restrict__ W,
-    int64_t ldw, int bytes_a, int bytes_b, int tiles_p, int tiles_q) {
+    float* __restrict__ C, int64_t ldc, const float* __restrict__ gamma, const uint32_t* __restrict__ mask,
+    int64_t kw, int bytes_a, int bytes_b, int tiles_p, int tiles_q) {
   constexpr int BK = 64;
   constexpr int ROWB = BK * 2;
   constexpr int THREADS = 64 * WM * WN;
@@ -321,7 +335,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
   int lcol = wn * (BN / WN) + lr;
   asm volatile("" : "+v"(lrow), "+v"(lcol));
   const float g = gamma[0];
-  const float d = __fadd_rn(g, kEps);
   if constexpr (EPI == 0) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -336,36 +349,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
         }
       }
   } else {
-    // The range mask of the tile goes into LDS first, one bit per output:
-    // vector-memory operations complete in order, so W loads interleaved
-    // with the output stores would each wait for the stores before them.
-    // Wave w reads W for tile rows [32 w, 32 w + 32), lane l holding columns
-    // 64 k + l; a ballot per (row, k) is that row's 64-column bit word.
-    constexpr int WPR = BN / 64;          // 64-bit words per tile row
-    constexpr int RPW = BM / (WM * WN);   // tile rows per wave
-    uint64_t* mbits = reinterpret_cast<uint64_t*>(smem);  // [BM][WPR]; every wave is past the last stage
-#pragma unroll 1
-    for (int r0 = wave * RPW; r0 < (wave + 1) * RPW; r0 += 4) {
-      float wv[4][WPR];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int64_t p = p0 + r0 + rr;
-#pragma unroll
-        for (int k = 0; k < WPR; ++k) {
-          const int64_t q = q0 + 64 * k + lane;
-          wv[rr][k] = (p < P && q < Q) ? W[p * ldw + q] : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int k = 0; k < WPR; ++k) {
-          const uint64_t bits = __ballot(fabsf(__fdiv_rn(wv[rr][k], d)) <= 1.0f);
-          if (lane == 0) mbits[(r0 + rr) * WPR + k] = bits;
-        }
+    // The tile's mask words go into LDS first (every wave is past the last
+    // stage's LDS reads): vector-memory operations complete in order, so
+    // mask loads interleaved with the output stores would each wait for the
+    // stores before them.
+    constexpr int WPR32 = BN / 32;  // mask words per tile row
+    uint32_t* mb = reinterpret_cast<uint32_t*>(smem);
+    const int64_t w0 = q0 >> 5;
+    for (int idx = tid; idx < BM * WPR32; idx += THREADS) {
+      const int row = idx / WPR32, wi = idx % WPR32;
+      const int64_t p = p0 + row, w = w0 + wi;
+      mb[idx] = (p < P && w < kw) ? mask[p * kw + w] : 0u;
     }
     __syncthreads();
-    const uint32_t* mb32 = reinterpret_cast<const uint32_t*>(smem);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -373,8 +369,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
         const int row = lrow + i * 32 + 8 * (e >> 2) + (e & 3);
         const int64_t p = p0 + row;
         if (p >= P) continue;
-        // bit lr of words (row, column block lcol / 32 + j): columns lcol + 32 j
-        const uint32_t* wrow = mb32 + row * (2 * WPR) + (lcol >> 5);
+        // bit lr of words (row, lcol / 32 + j): columns lcol + 32 j
+        const uint32_t* wrow = mb + row * WPR32 + (lcol >> 5);
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           const int64_t q = q0 + lcol + j * 32;
@@ -387,11 +383,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
 
 template <int BM, int BN, int WM, int WN, int BMODE, int EPI>
 void launch_gemm(const uint16_t* A, int64_t P, int64_t lda, const void* B, int64_t Q, int64_t Rp, float* C,
-                 int64_t ldc, const float* gamma, const float* W, int64_t ldw, int bytes_a, int bytes_b,
+                 int64_t ldc, const float* gamma, const uint32_t* mask, int64_t kw, int bytes_a, int bytes_b,
                  hipStream_t stream) {
   const int tiles_p = static_cast<int>((P + BM - 1) / BM), tiles_q = static_cast<int>((Q + BN - 1) / BN);
   bf16_gemm_nt_kernel<BM, BN, WM, WN, BMODE, EPI><<<static_cast<unsigned>(tiles_p * tiles_q), 64 * WM * WN, 0,
-                                                    stream>>>(A, P, lda, B, Q, Rp, C, ldc, gamma, W, ldw, bytes_a,
+                                                    stream>>>(A, P, lda, B, Q, Rp, C, ldc, gamma, mask, kw, bytes_a,
                                                               bytes_b, tiles_p, tiles_q);
 }
 
@@ -406,15 +402,15 @@ size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma, uint32_t* packedT,
-                                  hipStream_t stream) {
+                                  uint32_t* mask, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((N + kTile - 1) / kTile), static_cast<unsigned>((K + kTile - 1) / kTile));
-  pack_transposed_kernel<<<grid, 256, 0, stream>>>(W, N, K, gamma, packedT, padded_k(N));
+  pack_transposed_kernel<<<grid, 256, 0, stream>>>(W, N, K, gamma, packedT, padded_k(N), mask, mask_words(K));
   return hipGetLastError();
 }
 
 hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, const uint32_t* packedT,
-                           const float* gamma, const int8_t* Xq, const float* gamma_a, const float* W, float* dX,
-                           float* dW, void* workspace, hipStream_t stream) {
+                           const float* gamma, const int8_t* Xq, const float* gamma_a, const uint32_t* mask,
+                           float* dX, float* dW, void* workspace, hipStream_t stream) {
   const int64_t Mp = ((M + 63) / 64) * 64, Np = padded_k(N), Kp = padded_k(K);
   char* ws = static_cast<char*>(workspace);
   uint16_t* dYp = reinterpret_cast<uint16_t*>(ws);
@@ -440,8 +436,8 @@ hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, 
     transpose_kernel<0><<<g0, 256, 0, stream>>>(dY, M, N, N, nullptr, dYt, Mp);
     const dim3 g1(static_cast<unsigned>((K + kTile - 1) / kTile), static_cast<unsigned>(Mp / kTile));
     transpose_kernel<1><<<g1, 256, 0, stream>>>(Xq, M, K, Kp, gamma_a, At, Mp);
-    launch_gemm<256, 256, 4, 2, 0, 1>(dYt, N, Mp, At, K, Mp, dW, K, gamma, W, K, static_cast<int>(N * Mp * 2),
-                                      static_cast<int>(K * Mp * 2), stream);
+    launch_gemm<256, 256, 4, 2, 0, 1>(dYt, N, Mp, At, K, Mp, dW, K, gamma, mask, mask_words(K),
+                                      static_cast<int>(N * Mp * 2), static_cast<int>(K * Mp * 2), stream);
   }
   return hipGetLastError();
 }

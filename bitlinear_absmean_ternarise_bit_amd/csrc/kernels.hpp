@@ -50,12 +50,14 @@ hipError_t launch_prefill_gemm(const int8_t* Xq, const float* gamma_a, const int
 hipError_t launch_lut_gemv(const int8_t* Xq, const float* gamma_a, int64_t M, int64_t K, const uint32_t* packed,
                            int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L, hipStream_t stream);
 
-// STE backward: codes of W^T (2-bit format, rows k) and the two bf16 GEMMs
+// STE backward: codes of W^T (2-bit format, rows k) and the range mask of W
+// (bits, mask_words(K) 32-bit words per row), then the two bf16 GEMMs
+inline int64_t mask_words(int64_t K) { return (K + 31) / 32; }
 hipError_t launch_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma, uint32_t* packedT,
-                                  hipStream_t stream);
+                                  uint32_t* mask, hipStream_t stream);
 size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, const uint32_t* packedT,
-                           const float* gamma, const int8_t* Xq, const float* gamma_a, const float* W, float* dX,
-                           float* dW, void* workspace, hipStream_t stream);
+                           const float* gamma, const int8_t* Xq, const float* gamma_a, const uint32_t* mask,
+                           float* dX, float* dW, void* workspace, hipStream_t stream);
 
 }  // namespace bitlinear

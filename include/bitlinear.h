@@ -253,13 +253,22 @@ int bitlinear_ffn_forward(int64_t L, const void* X, int x_dtype, int64_t M, int6
  * results differ from exact sums by float32 accumulation rounding.
  */
 
-/* Codes of W^T for the backward's dX: the same ternary codes (same gamma,
- * computed by bitlinear_quantize_weights on W) transposed, as a [K, N] matrix
- * in the 2-bit packed format of this file (bitlinear_packed_bytes(K, N) bytes).
- * W: device float32 [N, K]; gamma: device float32[1]; packedT: device,
- * 16-byte aligned. */
+/* Bytes of the range mask of an [N, K] weight matrix: N rows of
+ * ceil(K / 32) 32-bit words. */
+size_t bitlinear_ste_mask_bytes(int64_t N, int64_t K);
+
+/* What the backward needs from W, formed once per weight update:
+ * packedT: the codes of W^T for dX, i.e. the same ternary codes (same gamma,
+ *   from bitlinear_quantize_weights on W) transposed, as a [K, N] matrix in the
+ *   2-bit packed format of this file (bitlinear_packed_bytes(K, N) bytes),
+ *   16-byte aligned;
+ * mask: the range mask for dW, bit k % 32 of word k / 32 of row n set iff
+ *   |fp32(W[n, k] / fp32(gamma + eps))| <= 1 (bits past K are 0),
+ *   bitlinear_ste_mask_bytes(N, K) bytes, 4-byte aligned.
+ * Either output may be NULL (not both).  W: device float32 [N, K];
+ * gamma: device float32[1]. */
 int bitlinear_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma,
-                              uint32_t* packedT, void* stream);
+                              uint32_t* packedT, uint32_t* mask, void* stream);
 
 /* Workspace bytes of bitlinear_backward: padded and transposed bf16 copies of
  * dY and A_hat (about 2 M (2N + K) bytes). */
@@ -270,7 +279,7 @@ size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * packedT: from bitlinear_pack_transposed (needed for dX).
  * Xq, gamma_a: the forward's activation codes [M, Kp] and scales [M], as
  *   bitlinear_quantize_activations writes them (needed for dW).
- * W: device float32 [N, K], the weights the codes came from (for dW's mask).
+ * mask: the range mask from bitlinear_pack_transposed (needed for dW).
  * dX: device float32 [M, K] or NULL;  dW: device float32 [N, K] or NULL
  *   (at least one).  workspace: >= bitlinear_backward_workspace_bytes(M, N, K),
  *   256-byte aligned.  Requires M*padded_k(N), N*M and K*M (M rounded up to 64)
@@ -278,7 +287,7 @@ size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
  */
 int bitlinear_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K,
                        const uint32_t* packedT, const float* gamma,
-                       const int8_t* Xq, const float* gamma_a, const float* W,
+                       const int8_t* Xq, const float* gamma_a, const uint32_t* mask,
                        float* dX, float* dW, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- radix-3 weights: five per byte ------------------------------------ */

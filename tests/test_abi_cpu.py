@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(abi.SIGNATURES)
@@ -115,6 +115,39 @@ def test_lut_checks(lib):
     assert call(ws=None) == abi.ERR_WORKSPACE
     assert call(wsb=ws - 1) == abi.ERR_WORKSPACE
     assert call(ws=P(4096 + 16)) == abi.ERR_ALIGN
+
+
+def test_backward_checks(lib):
+    assert lib.bitlinear_ste_mask_bytes(3, 33) == 3 * 2 * 4
+    assert lib.bitlinear_ste_mask_bytes(5, 64) == 5 * 2 * 4
+    assert lib.bitlinear_ste_mask_bytes(0, 64) == 0
+    pt = lib.bitlinear_pack_transposed
+    #   W, N, K, gamma, packedT, mask, stream
+    assert pt(None, 4, 4, FAKE, FAKE, FAKE, None) == abi.ERR_NULL
+    assert pt(FAKE, 4, 4, FAKE, None, None, None) == abi.ERR_NULL  # neither output
+    assert pt(FAKE, 0, 4, FAKE, FAKE, FAKE, None) == abi.ERR_SHAPE
+    assert pt(FAKE, 4, 4, FAKE, P(4104), None, None) == abi.ERR_ALIGN
+    assert pt(FAKE, 4, 4, FAKE, None, P(4098), None) == abi.ERR_ALIGN
+    bw = lib.bitlinear_backward
+    ws = lib.bitlinear_backward_workspace_bytes(4, 8, 8)
+    #   dY, M, N, K, packedT, gamma, Xq, gamma_a, mask, dX, dW, ws, ws_bytes, stream
+    args = [FAKE, 4, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["dY", "M", "N", "K", "pT", "g", "Xq", "ga", "mask", "dX", "dW", "ws", "wsb", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return bw(*a)
+
+    assert call(dY=None) == abi.ERR_NULL
+    assert call(dX=None, dW=None) == abi.ERR_NULL
+    assert call(pT=None) == abi.ERR_NULL                 # dX needs the transposed codes
+    assert call(mask=None) == abi.ERR_NULL               # dW needs the range mask
+    assert call(M=0) == abi.ERR_SHAPE
+    assert call(mask=P(4098)) == abi.ERR_ALIGN
+    assert call(ws=None) == abi.ERR_WORKSPACE
+    assert call(wsb=ws - 1) == abi.ERR_WORKSPACE
 
 
 def test_ffn_checks(lib):

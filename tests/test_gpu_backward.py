@@ -1,7 +1,7 @@
 """STE backward on the GPU (through the C ABI) against the oracle.
 
-Bit-exact: the transposed packed codes and the positions where dW is masked to
-zero.  dX and dW: the products dY * code and dY * A_hat are exact in float32
+Bit-exact: the transposed packed codes, the range-mask bits and the positions
+where dW is masked to zero.  dX and dW: the products dY * code and dY * A_hat are exact in float32
 and the GPU sums them in float32 (bf16 matrix cores), so each result may differ
 from the oracle's exact sum by at most L * 2^-24 * sum|products| (L = the
 contraction length, one rounding per addition) plus one final rounding.
@@ -51,9 +51,9 @@ def setup(M, K, N, seed, outside=0.1):
     packed, gamma = bl.quantize_weights(Wd)
     X = torch.from_numpy(P.X_bf16_bits.view(np.int16)).to(DEV).view(torch.bfloat16)
     Xq, ga, _ = bl.quantize_activations(X)
-    packedT = bl.pack_transposed(Wd, gamma)
+    packedT, mask = bl.pack_transposed(Wd, gamma)
     dYd = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
-    return P, W, dY, Wd, gamma, Xq, ga, packedT, dYd
+    return P, W, dY, gamma, Xq, ga, packedT, mask, dYd
 
 
 @pytest.mark.parametrize("N,K", [(1, 1), (70, 33), (129, 300), (640, 1000), (16, 4097)])
@@ -62,11 +62,18 @@ def test_pack_transposed_bit_exact(N, K):
     P = random_problem(1, K, N, seed=N * K)
     W = torch.from_numpy(P.W).to(DEV)
     packed, gamma = bl.quantize_weights(W)
-    pT = bl.pack_transposed(W, gamma)
+    Wm = P.W.copy()
+    Wm[::3] *= 3.0  # some weights outside the clip range: mask bits 0
+    Wm_d = torch.from_numpy(Wm).to(DEV)
+    pT, mask = bl.pack_transposed(Wm_d, gamma)
+    pT_only, _ = bl.pack_transposed(Wm_d, gamma)
     torch.cuda.synchronize()
     g, q, _ = O.quantize_weights(P.W)
     assert pT.shape == (K, bl.packed_words(N))
-    assert np.array_equal(pT.cpu().numpy().view(np.uint32), O.pack_codes(np.ascontiguousarray(q.T)))
+    qm = O.ternary_codes(Wm, g)  # the codes of Wm under P.W's gamma
+    assert np.array_equal(pT.cpu().numpy().view(np.uint32), O.pack_codes(np.ascontiguousarray(qm.T)))
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32), O.pack_mask_bits(O.ste_weight_mask(Wm, g)))
+    assert torch.equal(pT, pT_only)
 
 
 BWD_CASES = [(1, 64, 64), (37, 300, 130), (128, 256, 192), (200, 1000, 520), (65, 130, 1100), (300, 64, 7)]
@@ -75,8 +82,8 @@ BWD_CASES = [(1, 64, 64), (37, 300, 130), (128, 256, 192), (200, 1000, 520), (65
 @pytest.mark.parametrize("M,K,N", BWD_CASES)
 def test_backward_parity(M, K, N):
     say(f"backward M={M} K={K} N={N}")
-    P, W, dY, Wd, gamma, Xq, ga, packedT, dYd = setup(M, K, N, seed=M + K + N)
-    dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, Wd)
+    P, W, dY, gamma, Xq, ga, packedT, mask, dYd = setup(M, K, N, seed=M + K + N)
+    dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, mask, K)
     torch.cuda.synchronize()
     g, q, _ = O.quantize_weights(W)
     rga, rxq, _ = O.absmax_quantize(P.X)
@@ -91,10 +98,10 @@ def test_backward_parity(M, K, N):
 
 
 def test_backward_one_output_at_a_time():
-    P, W, dY, Wd, gamma, Xq, ga, packedT, dYd = setup(50, 200, 90, seed=7)
-    dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, Wd)
-    dX1, n1 = bl.backward(dYd, packedT, gamma, Xq, ga, Wd, need_dw=False)
-    n2, dW2 = bl.backward(dYd, packedT, gamma, Xq, ga, Wd, need_dx=False)
+    P, W, dY, gamma, Xq, ga, packedT, mask, dYd = setup(50, 200, 90, seed=7)
+    dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, mask, 200)
+    dX1, n1 = bl.backward(dYd, packedT, gamma, Xq, ga, mask, 200, need_dw=False)
+    n2, dW2 = bl.backward(dYd, packedT, gamma, Xq, ga, mask, 200, need_dx=False)
     torch.cuda.synchronize()
     assert n1 is None and n2 is None
     assert torch.equal(dX, dX1) and torch.equal(dW, dW2)
@@ -104,8 +111,8 @@ def test_backward_7b_ffn_shape_sampled():
     # the 7B-like prefill projection (2048 x 4096 -> 11008): sampled rows of dX and dW
     M, K, N = 2048, 4096, 11008
     say(f"backward {M}x{K}x{N} (sampled)")
-    P, W, dY, Wd, gamma, Xq, ga, packedT, dYd = setup(M, K, N, seed=11, outside=0.05)
-    dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, Wd)
+    P, W, dY, gamma, Xq, ga, packedT, mask, dYd = setup(M, K, N, seed=11, outside=0.05)
+    dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, mask, K)
     torch.cuda.synchronize()
     g, q, _ = O.quantize_weights(W)
     rga, rxq, _ = O.absmax_quantize(P.X)
@@ -132,5 +139,6 @@ def test_backward_errors():
     with pytest.raises(bl.BitLinearError) as e:
         bl.backward(z, torch.zeros((4, 4), dtype=torch.int32, device=DEV), g,
                     torch.zeros((4, 64), dtype=torch.int8, device=DEV), g.repeat(4),
-                    torch.zeros((4, 4), device=DEV), workspace=torch.empty((16,), dtype=torch.uint8, device=DEV))
+                    torch.zeros((4, 1), dtype=torch.int32, device=DEV), 4,
+                    workspace=torch.empty((16,), dtype=torch.uint8, device=DEV))
     assert e.value.status == abi.ERR_WORKSPACE
