@@ -163,7 +163,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
   constexpr int A_LOADS = BM * 8 / THREADS;
   constexpr int B_LOADS = BMODE == 0 ? BN * 8 / THREADS : 1;
   static_assert(BM / WM == 64 && A_LOADS >= 1 && B_LOADS >= 1 && NI >= 1, "tile shape");
-  static_assert(BMODE == 0 || BN <= THREADS, "one packed row per thread");
+  static_assert(BMODE == 0 || THREADS == 4 * BN, "packed B: one 32-bit word of a row's unit per thread");
   __shared__ __align__(1024) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -212,9 +212,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
       b_dst[i] = A_BYTES + r * ROWB + 16 * (c ^ ((r >> 1) & 7));
     }
   }
-  // packed B: thread tid < BN stages row tid (one 16-byte unit of 64 codes)
+  // packed B: thread tid stages word tid % 4 of row tid / 4's unit (16 codes,
+  // two 16-byte slots of bf16), so the expansion is spread over every wave
   const uint32_t units = static_cast<uint32_t>(Rp >> 6);
-  const bool pb_row = tid < BN && q0 + tid < Q;
+  const int pb_r = tid >> 2, pb_w = tid & 3;
+  const bool pb_row = BMODE == 1 && q0 + pb_r < Q;
 
   v4u ra[2][A_LOADS], rb[2][B_LOADS];
   auto gload = [&](int it, auto set_tag) {
@@ -228,10 +230,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
         rb[S][i] =
             __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, b_off[i] == kOff ? kOff : b_off[i] + 128u * it, 0, 0);
     } else {
-      const uint32_t off = pb_row ? unit_offset(static_cast<uint32_t>(q0 + tid), static_cast<uint32_t>(it),
-                                                static_cast<uint32_t>(Q), units)
+      const uint32_t off = pb_row ? unit_offset(static_cast<uint32_t>(q0 + pb_r), static_cast<uint32_t>(it),
+                                                static_cast<uint32_t>(Q), units) + 4u * pb_w
                                   : kOff;
-      if (tid < BN) rb[S][0] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, off, 0, 0);
+      rb[S][0][0] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_b, off, 0, 0);
     }
   };
   auto swrite = [&](char* st, auto set_tag) {
@@ -241,19 +243,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
     if constexpr (BMODE == 0) {
 #pragma unroll
       for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<v4u*>(st + b_dst[i]) = rb[S][i];
-    } else if (tid < BN) {
-      // 64 codes -> 64 bf16 values c - 1 through two byte tables (v_perm):
+    } else {
+      // 16 codes -> 16 bf16 values c - 1 through two byte tables (v_perm):
       // high bytes {0xBF, 0x00, 0x3F} and low bytes {0x80, 0x00, 0x80} for c = 0, 1, 2
       constexpr uint32_t kHi = 0x003F00BFu, kLo = 0x00800080u;
-      const int r = tid;
+      const int r = pb_r;
       char* sb = st + A_BYTES + r * ROWB;
+      const uint32_t w = rb[S][0][0];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {  // slot c: k = 8c .. 8c + 7 = word c/2, fields i = 2(c%2), 2(c%2)+1
-        const uint32_t w = rb[S][0][c >> 1];
+      for (int cc = 0; cc < 2; ++cc) {  // slot c = 2 pb_w + cc: k = 8c .. 8c + 7, fields i = 2 cc, 2 cc + 1
+        const int c = 2 * pb_w + cc;
         v4u out;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint32_t x = (w >> (2 * (2 * (c & 1) + h))) & 0x03030303u;
+          const uint32_t x = (w >> (2 * (2 * cc + h))) & 0x03030303u;
           const uint32_t hi = __builtin_amdgcn_perm(0u, kHi, x);
           const uint32_t lo = __builtin_amdgcn_perm(0u, kLo, x);
           out[2 * h] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
