@@ -101,6 +101,11 @@ __global__ __launch_bounds__(256) void pad_rows_bf16_kernel(const uint16_t* __re
 // Transposes of the M-major operands into rows of Mp (zero-padded) entries:
 //   MODE 0: dst[n, m] = dY[m, n]                          (src bf16 [M, N])
 //   MODE 1: dst[k, m] = bf16(fp32(fp32(gamma_A[m] / 127) * Xq[m, k]))  (Xq int8 [M, ld])
+// 64 x 64 tiles through LDS with 16-byte global accesses: a source chunk is
+// 8 bf16 (MODE 0) or 16 int8 (MODE 1) of one row, read whole when it lies
+// inside the row and is 16-byte aligned, else element by element; an output
+// chunk is 8 consecutive m of one row of dst (Mp is a multiple of 64, so
+// always whole).
 template <int MODE>
 __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__ src, int64_t M, int64_t R,
                                                         int64_t ld, const float* __restrict__ gamma_a,
@@ -109,26 +114,59 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTile;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kTile;
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < kTile * kTile; idx += 256) {
-    const int ml = idx >> 6, rl = idx & 63;
+  constexpr int PER = MODE == 0 ? 8 : 16;          // source elements per 16-byte chunk
+  constexpr int CPR = kTile / PER;                 // chunks per tile row
+  constexpr int esize = MODE == 0 ? 2 : 1;
+  for (int idx = tid; idx < kTile * CPR; idx += 256) {
+    const int ml = idx / CPR, rl = (idx % CPR) * PER;
     const int64_t m = m0 + ml, r = r0 + rl;
-    uint16_t v = 0;
-    if (m < M && r < R) {
+    uint16_t v[PER];
+    if (m < M && r + PER <= R && ((m * ld + r) * esize) % 16 == 0) {
+      const uint4 c = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + (m * ld + r) * esize);
+      const uint32_t u[4] = {c.x, c.y, c.z, c.w};
       if constexpr (MODE == 0) {
-        v = static_cast<const uint16_t*>(src)[m * ld + r];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = static_cast<uint16_t>(u[i >> 1] >> (16 * (i & 1)));
       } else {
-        const float c = __fdiv_rn(gamma_a[m], 127.0f);
-        const int8_t q = static_cast<const int8_t*>(src)[m * ld + r];
-        v = f32_to_bf16_rne(__fmul_rn(c, static_cast<float>(q)));
+        const float sc = __fdiv_rn(gamma_a[m], 127.0f);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int8_t q = static_cast<int8_t>(u[i >> 2] >> (8 * (i & 3)));
+          v[i] = f32_to_bf16_rne(__fmul_rn(sc, static_cast<float>(q)));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        uint16_t e = 0;
+        if (m < M && r + i < R) {
+          if constexpr (MODE == 0) {
+            e = static_cast<const uint16_t*>(src)[m * ld + r + i];
+          } else {
+            const float sc = __fdiv_rn(gamma_a[m], 127.0f);
+            e = f32_to_bf16_rne(__fmul_rn(sc, static_cast<float>(static_cast<const int8_t*>(src)[m * ld + r + i])));
+          }
+        }
+        v[i] = e;
       }
     }
-    tile[ml][rl] = v;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) tile[ml][rl + i] = v[i];
   }
   __syncthreads();
-  for (int idx = tid; idx < kTile * kTile; idx += 256) {
-    const int rl = idx >> 6, ml = idx & 63;
-    const int64_t m = m0 + ml, r = r0 + rl;
-    if (r < R && m < Mp) dst[r * Mp + m] = tile[ml][rl];
+  // output chunk (row r, m = 8 c .. 8 c + 7); eight consecutive threads
+  // write one row's 128 contiguous bytes
+  for (int idx = tid; idx < kTile * (kTile / 8); idx += 256) {
+    const int rl = idx >> 3, c = idx & 7;
+    const int64_t r = r0 + rl;
+    if (r >= R) continue;
+    uint4 out;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(tile[8 * c + 2 * i][rl]) | (static_cast<uint32_t>(tile[8 * c + 2 * i + 1][rl]) << 16);
+    out.x = w[0]; out.y = w[1]; out.z = w[2]; out.w = w[3];
+    if (m0 + 8 * c < Mp) *reinterpret_cast<uint4*>(dst + r * Mp + m0 + 8 * c) = out;
   }
 }
 
