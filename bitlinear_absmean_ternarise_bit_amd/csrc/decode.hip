@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 // workgroups (2 per CU) when the work allows and wastes at most 1/16 of a
 // layer in its last block.
 int pick_groups(int64_t L, int64_t N) {
-  for (int gsz = 16; gsz > 1; gsz >>= 1) {
+  for (int gsz = 64; gsz > 1; gsz >>= 1) {
     const int64_t rows = int64_t(kWaves) * kRowsPerWave * gsz;
     const int64_t bpl = (N + rows - 1) / rows;
     if (L * bpl >= 512 && (bpl * rows - N) * 16 <= N) return gsz;
