@@ -165,6 +165,7 @@ FORWARD_CASES = [
     (2000, 1050, 6200, "f32", "prefill"),   # 256 x 256 tiles, ragged M, N and a half K stage
     (2048, 200, 11008, "bf16", "prefill"),  # 1.34 rounds of big tiles: columns split over two launches
     (2048, 200, 11000, "f32", "prefill"),   # same split, ragged N: partial last row block in the second
+    (1, 65472, 64, "bf16", "decode"),       # the longest row the decode path holds on chip (Kp + 16 = 65488)
 ]
 
 
@@ -177,6 +178,40 @@ PERSISTENT_CASES = [
     (4096, 100, 5120, "bf16"),   # one stage per tile
     (4096, 64, 5120, "f32"),     # a single half stage per tile
 ]
+
+
+def test_prefill_largest_k():
+    """K = 2^20, the largest the library accepts: 16384 stages per tile and
+    accumulators up to 127 * 2^20 in magnitude, still exact in INT32."""
+    M, K, N = 20, 1 << 20, 50
+    say(f"prefill largest K M={M} K={K} N={N}")
+    P = random_problem(M, K, N, seed=7, x_dtype="f32")
+    packed, gamma, Y, acc = run_full(P, path="prefill")
+    ref = O.bitlinear_forward(P.X, P.W)
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    check_y(Y.cpu().numpy(), ref["Y"])
+
+
+def test_prefill_token_chunks():
+    """M * Kp above 2^31 code bytes: the GEMM runs the tokens in chunks (its
+    buffer offsets are 32-bit).  X is a seeded 64-token block repeated down
+    33000 rows, so every output row has an oracle value: that of its row in
+    the block.  The chunk boundary (row 32640 with 128-row tiles) lies inside
+    the range, and so does a ragged last tile."""
+    R, K, N, M = 64, 65536, 64, 33000
+    assert M * K > 2 ** 31
+    say(f"prefill token chunks M={M} K={K} N={N}")
+    P = random_problem(R, K, N, seed=11, x_dtype="bf16")
+    ref = O.bitlinear_forward(P.X, P.W)
+    W = torch.from_numpy(P.W).to(DEV)
+    X = dev_x(P).repeat((M + R - 1) // R, 1)[:M].contiguous()
+    packed, gamma = bl.quantize_weights(W)
+    Y, acc = bl.forward(X, packed, gamma, K, path="prefill", return_acc=True)
+    torch.cuda.synchronize()
+    del X
+    rows = np.arange(M) % R
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"][rows])
+    check_y(Y.cpu().numpy(), ref["Y"][rows])
 
 
 @pytest.mark.parametrize("M,K,N,dt", PERSISTENT_CASES)
