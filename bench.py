@@ -31,6 +31,11 @@ Weight quantisation (absmean + ternarise + pack) runs once per weight matrix
 before the timed region; it is timed separately and reported under
 "weight_quantisation".
 
+Every line also carries "attainable": what plain kernels reach on this GPU
+(a 1 GiB streaming read, a streaming copy, back-to-back INT8 MFMAs on
+registers) beside the published peaks that "roofline" uses (--no-peaks skips
+them), and the CPU baseline names the host's CPU model.
+
 Prints exactly one JSON line on stdout; progress goes to stderr.
 --copy-calibration runs a plain 1 GiB device copy (for HBM counter scaling).
 """
@@ -578,6 +583,57 @@ def cpu_baseline_backward(P, seconds):
 
 # ---------------------------------------------------------------------------
 
+def attainable_peaks(torch, bl, dev, read_blocks: int = 2048, mfma_iters: int = 20000) -> dict:
+    """The chip's attainable rates for plain kernels, beside the published peaks:
+    a 1 GiB streaming read (16-byte nontemporal loads, one contiguous slice per
+    workgroup), a 512 MiB -> 512 MiB streaming copy, and back-to-back INT8
+    MFMAs on registers (two workgroups per CU)."""
+    lib = bl.abi.load()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    out = torch.empty(read_blocks * 256, dtype=torch.int32, device=dev)
+
+    def timed(fn, reps=10):
+        for _ in range(2):
+            fn()
+        with Timer(torch) as t:
+            for _ in range(reps):
+                fn()
+        return t.ms / reps
+
+    def call(name, st):
+        bl.abi.check(name, st)
+
+    ms_read = timed(lambda: call("bitlinear_probe_stream", lib.bitlinear_probe_stream(
+        buf.data_ptr(), None, nbytes, read_blocks, out.data_ptr(), stream)))
+    half = buf.view(2, -1)
+    ms_copy = timed(lambda: call("bitlinear_probe_stream", lib.bitlinear_probe_stream(
+        half[0].data_ptr(), half[1].data_ptr(), nbytes // 2, read_blocks // 2, None, stream)))
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    mout = torch.empty(2 * cus * 256, dtype=torch.int32, device=dev)
+    ms_mfma = timed(lambda: call("bitlinear_probe_mfma_i8", lib.bitlinear_probe_mfma_i8(
+        mfma_iters, 2 * cus, mout.data_ptr(), stream)), reps=3)
+    ops = 2 * cus * 4 * 8 * mfma_iters * 65536
+    del buf, out, mout
+    return {"hbm_read_GBps": round(nbytes / ms_read / 1e6, 1),
+            "hbm_copy_GBps": round(nbytes / ms_copy / 1e6, 1),
+            "mfma_i8_TOPS": round(ops / ms_mfma / 1e9, 1),
+            "note": "plain kernels on this GPU: 1 GiB streaming read; 512 MiB copy (GB/s of bytes read "
+                    "+ written); independent v_mfma_i32_32x32x32_i8 on registers"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def copy_calibration(torch, dev):
     n = (1 << 30) // 4
     src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -604,6 +660,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip the attainable-peak probes (streaming read and copy, register MFMAs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -637,7 +695,13 @@ def main():
             "vs_baseline": None, "dtype": out.pop("dtype"), "data": "synthetic (seeded)",
             "config": out.pop("config")}
     line.update(out)
+    if "cpu_baseline" in line:
+        line["cpu_baseline"]["cpu_model"] = cpu_model()
+    if args.peaks:
+        line["attainable"] = attainable_peaks(torch, bl, dev)
+    props = torch.cuda.get_device_properties(dev)
     line["device"] = torch.cuda.get_device_name(dev)
+    line["device_cus"] = props.multi_processor_count
     print(json.dumps(line), flush=True)
 
 

@@ -43,6 +43,8 @@ SIGNATURES = {
     "bitlinear_forward": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _sz, _p]),
     "bitlinear_forward_ex": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _int, _p, _sz, _p]),
     "bitlinear_forward_quantized": (_int, [_p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p]),
+    "bitlinear_probe_stream": (_int, [_p, _p, _i64, _int, _p, _p]),
+    "bitlinear_probe_mfma_i8": (_int, [_int, _int, _p, _p]),
     "bitlinear_forward_batched": (_int, [_i64, _p, _int, _i64, _i64, _p, _i64, _p, _p, _p]),
     "bitlinear_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "bitlinear_ffn_forward": (_int, [_i64, _p, _int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int,

@@ -353,6 +353,23 @@ int bitlinear_forward_lut(int64_t L, const void* X, int x_dtype, int64_t M, int6
   return hip_status(launch_lut_gemv(w.xq, w.ga, M, K, packed, N, gamma, Y, acc, L, s));
 }
 
+int bitlinear_probe_stream(const void* src, void* dst, int64_t bytes, int blocks, uint32_t* out, void* stream) {
+  if (!src || (!dst && !out)) return BITLINEAR_ERR_NULL;
+  if (blocks < 1 || blocks > (1 << 20) || bytes < 1 || bytes % (int64_t(blocks) * 32768) != 0 ||
+      bytes / blocks >= (int64_t(1) << 31))
+    return BITLINEAR_ERR_SHAPE;
+  if (!aligned(src, 16) || (dst && !aligned(dst, 16)) || (out && !aligned(out, 4))) return BITLINEAR_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(dst ? launch_probe_copy(src, dst, bytes, blocks, s) : launch_probe_read(src, bytes, blocks, out, s));
+}
+
+int bitlinear_probe_mfma_i8(int iters, int blocks, int32_t* out, void* stream) {
+  if (!out) return BITLINEAR_ERR_NULL;
+  if (iters < 1 || blocks < 1 || blocks > (1 << 20)) return BITLINEAR_ERR_SHAPE;
+  if (!aligned(out, 4)) return BITLINEAR_ERR_ALIGN;
+  return hip_status(launch_probe_mfma_i8(iters, blocks, out, static_cast<hipStream_t>(stream)));
+}
+
 const char* bitlinear_status_string(int status) {
   switch (status) {
     case BITLINEAR_OK: return "ok";

@@ -60,4 +60,10 @@ hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, 
                            const float* gamma, const int8_t* Xq, const float* gamma_a, const uint32_t* mask,
                            float* dX, float* dW, void* workspace, hipStream_t stream);
 
+// attainable-peak probes (measurement only): a streaming read of `bytes` (one
+// word per thread to `out`), a streaming copy, and back-to-back INT8 MFMAs
+hipError_t launch_probe_read(const void* src, int64_t bytes, int blocks, uint32_t* out, hipStream_t stream);
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t stream);
+hipError_t launch_probe_mfma_i8(int iters, int blocks, int32_t* out, hipStream_t stream);
+
 }  // namespace bitlinear

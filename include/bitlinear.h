@@ -373,6 +373,31 @@ int bitlinear_forward_lut(int64_t L, const void* X, int x_dtype, int64_t M, int6
                           float* Y, int32_t* acc, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* ---- measurement hooks (not part of the method) --------------------------- */
+/*
+ * What the chip delivers to plain kernels, reported beside the published
+ * peaks (8 TB/s HBM3E, 5 POPS dense INT8) by the benchmark.
+ *
+ * bitlinear_probe_stream: `blocks` 256-thread workgroups each stream one
+ * contiguous slice of `bytes` / `blocks` bytes from src with 16-byte
+ * streaming loads (eight per lane in flight, one KiB per wave per load).
+ * dst != NULL: the slices are copied to dst (`bytes` written); else each
+ * thread folds what it read into one word of out (blocks * 256 uint32).
+ * Requires bytes a multiple of 32768 * blocks, bytes / blocks < 2^31,
+ * 1 <= blocks <= 2^20; src and dst 16-byte aligned, out 4-byte aligned.
+ *
+ * bitlinear_probe_mfma_i8: `blocks` 256-thread workgroups (two per CU), each
+ * wave issuing 8 * iters v_mfma_i32_32x32x32_i8 (65536 operations each) on
+ * eight independent register accumulators, no memory traffic; each thread
+ * writes one word of out (blocks * 256 int32).  Operations per call:
+ * blocks * 4 * 8 * iters * 65536.
+ *
+ * Errors: BITLINEAR_ERR_NULL, _SHAPE, _ALIGN, _HIP.
+ */
+int bitlinear_probe_stream(const void* src, void* dst, int64_t bytes, int blocks, uint32_t* out,
+                           void* stream);
+int bitlinear_probe_mfma_i8(int iters, int blocks, int32_t* out, void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* bitlinear_status_string(int status);
 

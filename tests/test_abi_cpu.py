@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(abi.SIGNATURES)
@@ -270,6 +270,19 @@ def test_forward_batched_checks(lib):
     assert f(4, FAKE, 1, 17, 2048, FAKE, 2048, FAKE, FAKE, None) == abi.ERR_SHAPE
     assert f(4, FAKE, 5, 1, 2048, FAKE, 2048, FAKE, FAKE, None) == abi.ERR_DTYPE
     assert f(4, FAKE, 1, 1, 2048, P(4100), 2048, FAKE, FAKE, None) == abi.ERR_ALIGN
+
+
+def test_probe_checks(lib):
+    s, m = lib.bitlinear_probe_stream, lib.bitlinear_probe_mfma_i8
+    assert s(None, FAKE, 1 << 20, 32, None, None) == abi.ERR_NULL
+    assert s(FAKE, None, 1 << 20, 32, None, None) == abi.ERR_NULL       # neither dst nor out
+    assert s(FAKE, FAKE, (1 << 20) + 16, 32, None, None) == abi.ERR_SHAPE  # not a multiple of 32 KiB per block
+    assert s(FAKE, FAKE, 1 << 20, 0, None, None) == abi.ERR_SHAPE
+    assert s(FAKE, FAKE, 1 << 32, 1, None, None) == abi.ERR_SHAPE       # a slice of 2^32 bytes
+    assert s(P(4100), FAKE, 1 << 20, 32, None, None) == abi.ERR_ALIGN
+    assert m(1, 1, None, None) == abi.ERR_NULL
+    assert m(0, 1, FAKE, None) == abi.ERR_SHAPE
+    assert m(1, 0, FAKE, None) == abi.ERR_SHAPE
 
 
 def test_header_documents_citations_and_conventions():

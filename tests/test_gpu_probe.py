@@ -1,0 +1,54 @@
+"""The attainable-peak probes (measurement hooks of the C ABI) touch exactly
+the bytes they are timed on: the streaming read folds every word of its slice
+(checked against a host emulation of the access pattern), the copy
+reproduces its source, and the MFMA loop is deterministic."""
+import numpy as np
+import pytest
+import torch
+
+import bitlinear_absmean_ternarise_bit_amd as bl
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def stream():
+    return torch.cuda.current_stream(DEV).cuda_stream
+
+
+def test_probe_stream_read_folds_every_word():
+    blocks, per_block = 6, 3 * 32768
+    rng = np.random.default_rng(5)
+    host = rng.integers(0, 2 ** 32, size=blocks * per_block // 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).to(DEV)
+    out = torch.zeros(blocks * 256, dtype=torch.int32, device=DEV)
+    lib = bl.abi.load()
+    bl.abi.check("probe", lib.bitlinear_probe_stream(src.data_ptr(), None, blocks * per_block, blocks,
+                                                      out.data_ptr(), stream()))
+    torch.cuda.synchronize()
+    # thread t of block b: wave w = t // 64, lane l = t % 64 reads the 16-byte
+    # vectors at w*8192 + l*16 + u*1024 + i*32768 (u < 8) of its slice
+    words = host.reshape(blocks, per_block // 32768, 4, 8, 64, 4)  # [b, i, w, u, l, 4 words]
+    expect = np.bitwise_xor.reduce(words, axis=(1, 3, 5))          # [b, w, l]
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), expect.reshape(-1))
+
+
+def test_probe_stream_copy():
+    n = 4 * 32768 * 5
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device=DEV)
+    dst = torch.zeros_like(src)
+    lib = bl.abi.load()
+    bl.abi.check("probe", lib.bitlinear_probe_stream(src.data_ptr(), dst.data_ptr(), n, 5, None, stream()))
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
+def test_probe_mfma_deterministic():
+    lib = bl.abi.load()
+    a = torch.empty(4 * 256, dtype=torch.int32, device=DEV)
+    b = torch.empty_like(a)
+    bl.abi.check("probe", lib.bitlinear_probe_mfma_i8(7, 4, a.data_ptr(), stream()))
+    bl.abi.check("probe", lib.bitlinear_probe_mfma_i8(7, 4, b.data_ptr(), stream()))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and bool((a != 0).any())
