@@ -35,12 +35,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-__device__ __forceinline__ uint32_t offset_code(float w, float d, bool valid) {
-  const float t = __fdiv_rn(w, d);
-  const float q = __builtin_rintf(fminf(fmaxf(t, -1.0f), 1.0f));
-  return valid ? static_cast<uint32_t>(static_cast<int>(q) + 1) : 1u;
-}
-
 // Codes of W^T ([K rows of Np = padded_k(N) codes]) in the 2-bit format and
 // its interleaved row order, and the range mask of W as bits (bit k % 32 of
 // word k / 32 of row n: |fp32(W[n, k] / fp32(gamma + eps))| <= 1; bits past K
@@ -53,7 +47,7 @@ __global__ __launch_bounds__(256) void pack_transposed_kernel(const float* __res
                                                               uint32_t* __restrict__ packedT, int64_t Np,
                                                               uint32_t* __restrict__ mask, int64_t Kw) {
   __shared__ uint8_t codes[kTile][kTile + 4];  // [k][n]
-  const float d = __fadd_rn(gamma[0], kEps);
+  const TernaryThresholds thr = ternary_thresholds(gamma[0]);  // codes and mask without a division
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTile;
   const int64_t k0 = static_cast<int64_t>(blockIdx.y) * kTile;
   const int tid = threadIdx.x;
@@ -62,9 +56,9 @@ __global__ __launch_bounds__(256) void pack_transposed_kernel(const float* __res
     const int64_t n = n0 + nl, k = k0 + kl;
     const bool valid = n < N && k < K;
     const float w = valid ? W[n * K + k] : 0.0f;
-    codes[kl][nl] = static_cast<uint8_t>(offset_code(w, d, n < N));
+    codes[kl][nl] = static_cast<uint8_t>(ternary_code(w, thr.nonzero, n < N));
     if (mask) {
-      const uint64_t bits = __ballot(valid && fabsf(__fdiv_rn(w, d)) <= 1.0f);
+      const uint64_t bits = __ballot(valid && fabsf(w) <= thr.in_range);
       if ((tid & 63) == 0 && n < N) {
         const int64_t wd = k0 >> 5;
         mask[n * Kw + wd] = static_cast<uint32_t>(bits);

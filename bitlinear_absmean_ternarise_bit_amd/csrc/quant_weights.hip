@@ -191,52 +191,71 @@ __global__ __launch_bounds__(256) void absmean_finalize_kernel(const unsigned lo
   gamma[0] = static_cast<float>(sum / count);
 }
 
-// Offset code c = q + 1 of one weight, q = Round(Clip(w / d, -1, 1)) with an
-// IEEE float32 division and round half to even; padding (valid false) is a
-// zero weight, c = 1.
-__device__ __forceinline__ uint32_t offset_code(float w, float d, bool valid) {
-  const float t = __fdiv_rn(w, d);
-  const float q = __builtin_rintf(fminf(fmaxf(t, -1.0f), 1.0f));
-  return valid ? static_cast<uint32_t>(static_cast<int>(q) + 1) : 1u;
-}
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Ternarise and pack.  Each lane turns four consecutive weights (k = 4f..4f+3)
 // into the four bytes' bit pair 2i of word f/4 (i = f%4); four adjacent lanes
 // OR their parts into one word, stored at its place in the interleaved row
-// order (unit_offset).
+// order (unit_offset).  The codes come from one comparison per weight with
+// the threshold of ternary_thresholds (no division).  A lane handles four
+// grid-stride items per round, their 16-byte loads (streaming: every weight
+// is read once) issued together; its (row, quad) position advances by the
+// stride without a division.
 template <bool VEC>
 __global__ __launch_bounds__(256) void ternarise_pack_kernel(const float* __restrict__ W, int64_t N,
                                                              int64_t K, int64_t Kp,
                                                              const float* __restrict__ gamma,
                                                              uint32_t* __restrict__ packed) {
-  const float d = __fadd_rn(gamma[0], kEps);
-  const int64_t quads_per_row = Kp >> 2;
-  const int64_t total = N * quads_per_row;  // a multiple of 16: groups of 4 lanes stay together
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t f = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; f < total; f += stride) {
-    const int64_t n = f / quads_per_row;
-    const int64_t kq = (f - n * quads_per_row) << 2;
-    const float* row = W + n * K;
-    float w[4];
-    if (VEC && kq + 3 < K) {
-      const float4 v = *reinterpret_cast<const float4*>(row + kq);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else {
+  constexpr int U = 4;
+  const float thr = ternary_thresholds(gamma[0]).nonzero;
+  const int64_t qpr = Kp >> 2;       // quads (four weights) per row
+  const int64_t total = N * qpr;     // a multiple of 16: groups of 4 lanes stay together
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;  // a multiple of 4
+  const int64_t row_step = stride / qpr, quad_step = stride - row_step * qpr;
+  int64_t f = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  int64_t n = f / qpr, q = f - n * qpr;
+  const int i = static_cast<int>(threadIdx.x & 3);
+  for (; f < total; f += U * stride) {
+    int64_t nu[U], qu[U];
+    float w[U][4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) w[b] = (kq + b < K) ? row[kq + b] : 0.0f;
+    for (int u = 0; u < U; ++u) {
+      nu[u] = n;
+      qu[u] = q;
+      const int64_t kq = q << 2;
+      const float* row = W + n * K;
+      if (f + u * stride < total) {
+        if (VEC && kq + 3 < K) {
+          const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(row + kq));
+          w[u][0] = v[0]; w[u][1] = v[1]; w[u][2] = v[2]; w[u][3] = v[3];
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) w[u][b] = (kq + b < K) ? row[kq + b] : 0.0f;
+        }
+      }
+      n += row_step;
+      q += quad_step;
+      if (q >= qpr) {
+        q -= qpr;
+        ++n;
+      }
     }
-    uint32_t part = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) part |= offset_code(w[b], d, kq + b < K) << (8 * b);
-    const int i = static_cast<int>(f & 3);
-    part <<= 2 * i;
-    part |= __shfl_xor(part, 1, 4);
-    part |= __shfl_xor(part, 2, 4);
-    if (i == 0) {
-      const uint32_t wi = static_cast<uint32_t>(kq >> 4);  // word of the row
-      const uint32_t off = unit_offset(static_cast<uint32_t>(n), wi >> 2, static_cast<uint32_t>(N),
-                                       static_cast<uint32_t>(Kp >> 6));
-      packed[(off >> 2) + (wi & 3u)] = part;
+    for (int u = 0; u < U; ++u) {
+      if (f + u * stride >= total) break;  // the same for all four lanes of a word
+      const int64_t kq = qu[u] << 2;
+      uint32_t part = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) part |= ternary_code(w[u][b], thr, kq + b < K) << (8 * b);
+      part <<= 2 * i;
+      part |= __shfl_xor(part, 1, 4);
+      part |= __shfl_xor(part, 2, 4);
+      if (i == 0) {
+        const uint32_t wi = static_cast<uint32_t>(kq >> 4);  // word of the row
+        const uint32_t off = unit_offset(static_cast<uint32_t>(nu[u]), wi >> 2, static_cast<uint32_t>(N),
+                                         static_cast<uint32_t>(Kp >> 6));
+        packed[(off >> 2) + (wi & 3u)] = part;
+      }
     }
   }
 }
@@ -250,7 +269,7 @@ __global__ __launch_bounds__(256) void ternarise_pack_r3_kernel(const float* __r
                                                                 int64_t K, int64_t words_per_row,
                                                                 const float* __restrict__ gamma,
                                                                 uint32_t* __restrict__ packed) {
-  const float d = __fadd_rn(gamma[0], kEps);
+  const float thr = ternary_thresholds(gamma[0]).nonzero;
   const int64_t total = N * words_per_row;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t f = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; f < total; f += stride) {
@@ -270,7 +289,7 @@ __global__ __launch_bounds__(256) void ternarise_pack_r3_kernel(const float* __r
         for (int b = 0; b < 4; ++b) w[b] = (k + b < K) ? row[k + b] : 0.0f;
       }
 #pragma unroll
-      for (int b = 0; b < 4; ++b) v[b] = 3u * v[b] + offset_code(w[b], d, k + b < K);
+      for (int b = 0; b < 4; ++b) v[b] = 3u * v[b] + ternary_code(w[b], thr, k + b < K);
     }
     uint32_t word = 0;
 #pragma unroll
@@ -314,7 +333,8 @@ hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_
   launch_gamma(W, N, K, gamma, workspace, stream);
   const int64_t Kp = padded_k(K);
   const int64_t total = N * (Kp / 4);
-  int64_t pblocks = (total + 255) / 256;
+  // four items per lane (the kernel's batch), at most 65536 workgroups
+  int64_t pblocks = (total + 1023) / 1024;
   if (pblocks > 65536) pblocks = 65536;
   if ((K & 3) == 0)
     ternarise_pack_kernel<true><<<static_cast<int>(pblocks), 256, 0, stream>>>(W, N, K, Kp, gamma, packed);
