@@ -296,11 +296,33 @@ def cpu_baseline_decode(P, layer_bytes, seconds, lut=False):
         if el >= seconds:
             break
     log(f"[bench] cpu oracle: {reps} forwards of layer 0 in {el:.1f} s")
-    return {"value": round(reps * layer_bytes / el / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
-            "kind": "oracle",
-            "sample": f"layer 0 of the pool ({P.name}, seed 0): the oracle's forward from ternary "
-                      f"codes (absmax quantise + {'LUT' if lut else 'exact'} contraction + rescale) "
-                      f"repeated {reps} times"}
+    out = {"value": round(reps * layer_bytes / el / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+           "kind": "oracle",
+           "sample": f"layer 0 of the pool ({P.name}, seed 0): the oracle's forward from ternary "
+                     f"codes (absmax quantise + {'LUT' if lut else 'exact'} contraction + rescale) "
+                     f"repeated {reps} times"}
+    if not lut:
+        out["naive_loop"] = cpu_naive_loop(P, q)
+    return out
+
+
+def cpu_naive_loop(P, q, seconds=3.0):
+    """The oracle's literal add / subtract / skip loop (pure Python, one core) on
+    layer 0's first token, output channel after output channel, for a few seconds."""
+    import oracle as O
+    _, Xq, _ = O.absmax_quantize(P.X)
+    xr = Xq[0].tolist()
+    done, t0 = 0, time.perf_counter()
+    while True:
+        O.zero_gemm_dot(xr, q[done % q.shape[0]].tolist())
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    log(f"[bench] cpu naive loop: {done} outputs in {el:.1f} s")
+    return {"value": round(done * P.K / el / 1e9, 6), "unit": "G weights/s", "cores": 1,
+            "kind": "oracle naive add/subtract/skip loop",
+            "sample": f"{done} outputs (token 0 against output channels 0..{min(done, q.shape[0]) - 1}, K={P.K})"}
 
 
 # ---------------------------------------------------------------------------
