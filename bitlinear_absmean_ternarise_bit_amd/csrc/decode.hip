@@ -130,8 +130,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   constexpr int kPerUnit = Format<FMT>::kPerUnit;
   constexpr int kMfma = Format<FMT>::kMfma;
   constexpr int kUnroll = Format<FMT>::kUnroll;
-  const int64_t layer = blockIdx.x / blocks_per_layer;
-  const int rb = static_cast<int>(blockIdx.x - layer * blocks_per_layer);
+  // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2:
+  // give each XCD a contiguous run of (layer, row block) pairs, so that the
+  // workgroups of one layer share one L2 (its tokens, or the FFN hidden
+  // layer, are fetched from memory once) and each XCD streams one region.
+  const uint32_t G = gridDim.x, G8 = G >> 3;
+  const uint32_t v = blockIdx.x < 8u * G8 ? (blockIdx.x & 7u) * G8 + (blockIdx.x >> 3) : blockIdx.x;
+  const int64_t layer = v / blocks_per_layer;
+  const int rb = static_cast<int>(v - layer * blocks_per_layer);
   const int64_t lds_stride = Kp + 16;  // +16 bytes: token rows start on different banks
   const int stage = stage_bytes(M, groups, EPI == kEpiAcc, M * lds_stride);  // per wave, 0: direct stores
   X = static_cast<const char*>(X) + layer * M * K * esize;

@@ -79,8 +79,13 @@ __global__ __launch_bounds__(kLutRows) void lut_gemv_kernel(
   constexpr int G = 16 * SU;          // blocks per slice
   __shared__ uint32_t tables[M * G * kLutStride];
   const int tid = threadIdx.x;
-  const int64_t layer = blockIdx.x / blocks_per_layer;
-  const uint32_t n = static_cast<uint32_t>(blockIdx.x % blocks_per_layer) * kLutRows + tid;
+  // workgroups are dealt round-robin to the 8 XCDs: give each XCD a
+  // contiguous run of (layer, row block) pairs, so a layer's workgroups share
+  // one L2 for its token codes
+  const uint32_t per_xcd = gridDim.x >> 3;
+  const uint32_t v = blockIdx.x < 8u * per_xcd ? (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3) : blockIdx.x;
+  const int64_t layer = v / blocks_per_layer;
+  const uint32_t n = static_cast<uint32_t>(v % blocks_per_layer) * kLutRows + tid;
   const uint32_t U = static_cast<uint32_t>(Kp >> 6);  // 16-byte units per row
   const uint32_t N32 = static_cast<uint32_t>(N);
   Xq += layer * M * Kp;
