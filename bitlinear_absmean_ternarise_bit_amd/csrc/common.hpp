@@ -70,28 +70,21 @@ __device__ __forceinline__ v4i unpack_word(uint32_t w) {
 
 // Ternary codes without a division.  [PMV] section 1: W_q = RoundClip(W / d)
 // with d = gamma + eps, here fp32(gamma + eps), an IEEE float32 quotient and
-// round half to even.  The code is +1 exactly when fp32(w / d) > 1/2 (a
-// quotient of exactly 1/2 rounds to 0), and fp32(x) > 1/2 exactly when the
-// real x exceeds 1/2 + 2^-25, the midpoint between 1/2 and the next float32,
-// which rounds to 1/2 (even).  So the code is nonzero exactly when
-// |w| > d (1/2 + 2^-25); that product is exact in float64, and as no float32
-// lies strictly between it and its float32 round-down t, the test is
-// |w| > t.  Likewise fp32(|w| / d) <= 1 exactly when |w| <= d (1 + 2^-24)
-// (the STE range mask).  Both thresholds are formed once per matrix.
-__device__ __forceinline__ float f32_round_down(double x) {  // x > 0, far from the float32 range ends
-  float f = static_cast<float>(x);
-  if (static_cast<double>(f) > x) f = __uint_as_float(__float_as_uint(f) - 1u);  // the next float32 below
-  return f;
-}
-
+// round half to even.  The code is nonzero exactly when fp32(|w| / d) > 1/2
+// (a quotient of exactly 1/2 rounds to 0), that is when the real |w| / d
+// exceeds 1/2 + 2^-25 (the tie above 1/2 rounds down to the even 1/2), that is
+// when |w| > d/2 + d 2^-25.  No float32 lies in (d/2, d/2 + d 2^-25]: d/2 is
+// exact and the float32 spacing there is larger than d 2^-25.  So for float32
+// weights the test is |w| > d/2.  Likewise fp32(|w| / d) <= 1 exactly when
+// |w| <= d (the STE range mask).
 struct TernaryThresholds {
-  float nonzero;  // |w| > nonzero  <=>  Round(Clip(fp32(w / d), -1, 1)) != 0
+  float nonzero;   // |w| > nonzero  <=>  Round(Clip(fp32(w / d), -1, 1)) != 0
   float in_range;  // |w| <= in_range  <=>  |fp32(w / d)| <= 1
 };
 
 __device__ __forceinline__ TernaryThresholds ternary_thresholds(float gamma) {
-  const double d = static_cast<double>(__fadd_rn(gamma, kEps));
-  return {f32_round_down(d * (0.5 + 0x1p-25)), f32_round_down(d * (1.0 + 0x1p-24))};
+  const float d = __fadd_rn(gamma, kEps);  // >= eps: d/2 is exact
+  return {__fmul_rn(d, 0.5f), d};
 }
 
 // Offset code c = q + 1 in {0, 1, 2} of one weight; padding (valid false) is
