@@ -166,6 +166,8 @@ FORWARD_CASES = [
     (2048, 200, 11008, "bf16", "prefill"),  # 1.34 rounds of big tiles: columns split over two launches
     (2048, 200, 11000, "f32", "prefill"),   # same split, ragged N: partial last row block in the second
     (1, 65472, 64, "bf16", "decode"),       # the longest row the decode path holds on chip (Kp + 16 = 65488)
+    (16, 3000, 333, "f32", "decode"),       # float32 rows over 4 KiB: the wave quantiser's two passes
+    (7, 8192, 200, "f32", "decode"),        # 32 KiB float32 rows, seven tokens over four waves
 ]
 
 
