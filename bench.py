@@ -687,7 +687,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(the BitLinear forward shards over tokens or output channels without changes to "
               "the kernel); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
