@@ -365,7 +365,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
   // epilogue: lane holds rows 8 (e / 4) + 4 lh + e % 4, column lr of each
   // 32 x 32 tile.  The lane's first row and column are opaque to the
   // compiler, so it does not compute the output addresses before the main
-  // loop and keep them live (spilled) across it.
+  // loop and keep them live (spilled) across it.  The outputs are written
+  // nontemporally: they are not read again here, and streaming them evicts
+  // less of the operand panels that other tiles on this XCD still read.
   int lrow = wm * 64 + 4 * lh;
   int lcol = wn * (BN / WN) + lr;
   asm volatile("" : "+v"(lrow), "+v"(lcol));
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           const int64_t q = q0 + lcol + j * 32;
-          if (q < Q) C[p * ldc + q] = __fmul_rn(acc[i][j][e], g);
+          if (q < Q) __builtin_nontemporal_store(__fmul_rn(acc[i][j][e], g), C + p * ldc + q);
         }
       }
   } else {
@@ -410,7 +412,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
         for (int j = 0; j < NI; ++j) {
           const int64_t q = q0 + lcol + j * 32;
           if (q >= Q) continue;
-          C[p * ldc + q] = (wrow[j] >> lr) & 1u ? acc[i][j][e] : 0.0f;
+          __builtin_nontemporal_store((wrow[j] >> lr) & 1u ? acc[i][j][e] : 0.0f, C + p * ldc + q);
         }
       }
   }

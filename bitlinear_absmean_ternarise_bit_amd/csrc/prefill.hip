@@ -326,7 +326,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
               const float r = fmaxf(y, 0.0f);
               y = __fmul_rn(r, r) + 0.0f;  // + 0: no negative zero
             }
-            Y[m * ldy + n] = y;
+            // Y streams past the caches (nontemporal), so it evicts less of
+            // the operand panels the other tiles on this XCD still read; the
+            // FFN hidden layer (EPI 2) is read again right away and is not
+            if constexpr (EPI == 2) Y[m * ldy + n] = y;
+            else __builtin_nontemporal_store(y, Y + m * ldy + n);
           }
         }
       }
