@@ -176,8 +176,10 @@ int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, 
 size_t bitlinear_ffn_workspace_bytes(int64_t L, int64_t M, int64_t D, int64_t F) {
   if (L < 1 || M < 1 || D < 1 || F < 1) return 0;
   const size_t hidden = align256(static_cast<size_t>(L) * static_cast<size_t>(M) * static_cast<size_t>(F) * 4);
-  const size_t codes = prefill_ws_bytes(M, D) > prefill_ws_bytes(M, F) ? prefill_ws_bytes(M, D)
-                                                                       : prefill_ws_bytes(M, F);
+  // codes of one layer's tokens (prefill path, both projections) or of all
+  // layers' hidden rows (decode path)
+  const size_t codes = prefill_ws_bytes(M, D) > prefill_ws_bytes(L * M, F) ? prefill_ws_bytes(M, D)
+                                                                           : prefill_ws_bytes(L * M, F);
   return hidden + codes;
 }
 
@@ -207,7 +209,7 @@ int bitlinear_ffn_forward(int64_t L, const void* X, int x_dtype, int64_t M, int6
   if (path == BITLINEAR_PATH_DECODE && !fits) return BITLINEAR_ERR_SHAPE;
   const bool decode = path == BITLINEAR_PATH_DECODE || (path == BITLINEAR_PATH_AUTO && fits);
   const size_t hidden_bytes = align256(static_cast<size_t>(L) * static_cast<size_t>(M) * static_cast<size_t>(F) * 4);
-  const size_t codes_bytes = decode ? 0
+  const size_t codes_bytes = decode ? prefill_ws_bytes(L * M, F)
                                     : (prefill_ws_bytes(M, D) > prefill_ws_bytes(M, F) ? prefill_ws_bytes(M, D)
                                                                                        : prefill_ws_bytes(M, F));
   const size_t need = (hidden ? 0 : hidden_bytes) + codes_bytes;
@@ -220,10 +222,14 @@ int bitlinear_ffn_forward(int64_t L, const void* X, int x_dtype, int64_t M, int6
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t up_words = F * (padded_k(D) / 16), down_words = D_out * (padded_k(F) / 16);
   if (decode) {
-    // all layers' hidden activations in one launch, then all down projections
+    // all layers' hidden activations in one launch, their codes in one
+    // quantiser launch (each hidden row once, instead of once in every
+    // workgroup of the down projection), then all down projections
+    PrefillWs w = prefill_ws(ws + (hidden ? 0 : hidden_bytes), L * M, F);
     hipError_t e = launch_decode(X, x_dtype, M, D, packed_up, F, gamma_up, A, nullptr, L, s, true);
+    if (e == hipSuccess) e = launch_act_quant(A, BITLINEAR_F32, L * M, F, w.xq, w.ga, w.rs, s);
     if (e != hipSuccess) return BITLINEAR_ERR_HIP;
-    return hip_status(launch_decode(A, BITLINEAR_F32, M, F, packed_down, D_out, gamma_down, Y, nullptr, L, s));
+    return hip_status(launch_decode_codes(w.xq, w.ga, w.rs, M, F, packed_down, D_out, gamma_down, Y, L, s));
   }
   PrefillWs w = prefill_ws(ws + (hidden ? 0 : hidden_bytes), M, D > F ? D : F);
   const int esize = x_dtype == BITLINEAR_F32 ? 4 : 2;

@@ -117,16 +117,20 @@ __host__ __device__ inline int stage_bytes(int M, int groups, bool with_acc, int
   return (M * groups * kRowsPerWave * 4 <= 4096 && code_bytes + kWaves * b <= 65536) ? b : 0;
 }
 
+// DT: 0 = float32 tokens, 1 = bfloat16 tokens, both quantised in phase A;
+// 2 = int8 codes [L, M, Kp] quantised beforehand, with gamma_A and the code
+// sums in ga_in / rs_in [L, M] (phase A only copies them into LDS).
 template <int FMT, int DT, bool VEC, int EPI>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const void* __restrict__ X, int M, int64_t K, int64_t Kp, int64_t units,
     const uint32_t* __restrict__ packed, int64_t N, const float* __restrict__ gamma,
-    float* __restrict__ Y, int32_t* __restrict__ acc, int blocks_per_layer, int groups) {
+    float* __restrict__ Y, int32_t* __restrict__ acc, int blocks_per_layer, int groups,
+    const float* __restrict__ ga_in, const int32_t* __restrict__ rs_in) {
   extern __shared__ __align__(16) int8_t sxq[];
   __shared__ float s_ga[kDecodeMaxM];
   __shared__ int s_rs[kDecodeMaxM];
 
-  constexpr int esize = DT == 0 ? 4 : 2;
+  constexpr int esize = DT == 0 ? 4 : DT == 1 ? 2 : 1;
   constexpr int kPerUnit = Format<FMT>::kPerUnit;
   constexpr int kMfma = Format<FMT>::kMfma;
   constexpr int kUnroll = Format<FMT>::kUnroll;
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const int rb = static_cast<int>(v - layer * blocks_per_layer);
   const int64_t lds_stride = Kp + 16;  // +16 bytes: token rows start on different banks
   const int stage = stage_bytes(M, groups, EPI == kEpiAcc, M * lds_stride);  // per wave, 0: direct stores
-  X = static_cast<const char*>(X) + layer * M * K * esize;
+  X = static_cast<const char*>(X) + layer * M * (DT == 2 ? Kp : K * esize);
   packed += layer * N * units * 4;
   Y += layer * M * N;
   if constexpr (EPI == kEpiAcc) acc += layer * M * N;
@@ -198,15 +202,38 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   load_batch(0, true, buf0);
   __builtin_amdgcn_sched_barrier(0);
 
-  // phase A: AbsMax INT8 codes of every token into LDS (one wave per token)
-  for (int m = wave; m < M; m += kWaves) {
-    float ga;
-    int rs;
-    quantize_row_wave<DT, VEC>(static_cast<const char*>(X) + m * K * esize, K, Kp, lane,
-                               sxq + m * lds_stride, ga, rs);
-    if (lane == 0) {
-      s_ga[m] = ga;
-      s_rs[m] = rs;
+  if constexpr (DT == 2) {
+    // phase A: copy the layer's codes (M rows of Kp bytes, contiguous) into
+    // the LDS rows, eight 16-byte loads per thread in flight
+    const uint4* src = static_cast<const uint4*>(X);
+    const int per_row = static_cast<int>(Kp >> 4);
+    const int total = M * per_row;
+    for (int i0 = threadIdx.x; i0 < total; i0 += 8 * kDecodeThreads) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[min(i0 + u * kDecodeThreads, total - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kDecodeThreads;
+        const int m = i / per_row;
+        if (i < total) *reinterpret_cast<uint4*>(sxq + m * lds_stride + 16 * (i - m * per_row)) = v[u];
+      }
+    }
+    if (threadIdx.x < M) {
+      s_ga[threadIdx.x] = ga_in[layer * M + threadIdx.x];
+      s_rs[threadIdx.x] = rs_in[layer * M + threadIdx.x];
+    }
+  } else {
+    // phase A: AbsMax INT8 codes of every token into LDS (one wave per token)
+    for (int m = wave; m < M; m += kWaves) {
+      float ga;
+      int rs;
+      quantize_row_wave<DT, VEC>(static_cast<const char*>(X) + m * K * esize, K, Kp, lane,
+                                 sxq + m * lds_stride, ga, rs);
+      if (lane == 0) {
+        s_ga[m] = ga;
+        s_rs[m] = rs;
+      }
     }
   }
   __syncthreads();
@@ -338,7 +365,7 @@ int pick_groups(int64_t L, int64_t N) {
 template <int FMT, int DT, bool VEC>
 hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed, int64_t N,
                     const float* gamma, float* Y, int32_t* acc, int64_t L, bool relu2,
-                    hipStream_t stream) {
+                    hipStream_t stream, const float* ga_in = nullptr, const int32_t* rs_in = nullptr) {
   const int64_t Kp = FMT == 2 ? padded_k(K) : r3_padded_k(K);
   const int64_t units = Kp / Format<FMT>::kPerUnit;
   const int groups = pick_groups(L, N);
@@ -350,19 +377,20 @@ hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed,
   const int64_t code_bytes = M * (Kp + 16);
   const size_t lds = static_cast<size_t>(code_bytes) +
                      static_cast<size_t>(kWaves) * stage_bytes(m, groups, with_acc, code_bytes);
-  if constexpr (FMT == 2) {
-    if (relu2) {
-      decode_kernel<FMT, DT, VEC, kEpiRelu2><<<blocks, kDecodeThreads, lds, stream>>>(
-          X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups);
-      return hipGetLastError();
-    }
-  }
-  if (acc)
-    decode_kernel<FMT, DT, VEC, kEpiAcc><<<blocks, kDecodeThreads, lds, stream>>>(
-        X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups);
-  else
+  if constexpr (DT == 2) {
     decode_kernel<FMT, DT, VEC, kEpiY><<<blocks, kDecodeThreads, lds, stream>>>(
-        X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups);
+        X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, ga_in, rs_in);
+  } else {
+    if (FMT == 2 && relu2)
+      decode_kernel<FMT, DT, VEC, FMT == 2 ? kEpiRelu2 : kEpiY><<<blocks, kDecodeThreads, lds, stream>>>(
+          X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, nullptr, nullptr);
+    else if (acc)
+      decode_kernel<FMT, DT, VEC, kEpiAcc><<<blocks, kDecodeThreads, lds, stream>>>(
+          X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, nullptr, nullptr);
+    else
+      decode_kernel<FMT, DT, VEC, kEpiY><<<blocks, kDecodeThreads, lds, stream>>>(
+          X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, nullptr, nullptr);
+  }
   return hipGetLastError();
 }
 
@@ -385,6 +413,12 @@ hipError_t launch_decode(const void* X, int x_dtype, int64_t M, int64_t K, const
                          int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
                          hipStream_t stream, bool relu2) {
   return launch_fmt<2>(X, x_dtype, M, K, packed, N, gamma, Y, acc, L, relu2, stream);
+}
+
+hipError_t launch_decode_codes(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum, int64_t M,
+                              int64_t K, const uint32_t* packed, int64_t N, const float* gamma, float* Y,
+                              int64_t L, hipStream_t stream) {
+  return launch_v<2, 2, true>(Xq, M, K, packed, N, gamma, Y, nullptr, L, false, stream, gamma_a, rowsum);
 }
 
 hipError_t launch_decode_r3(const void* X, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,

@@ -34,6 +34,12 @@ hipError_t launch_decode(const void* X, int x_dtype, int64_t M, int64_t K, const
                          int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,
                          hipStream_t stream, bool relu2 = false);
 
+// a4 + a6 (decode kernel) on codes from launch_act_quant: L layers of M
+// tokens, rows l * M .. l * M + M - 1 of Xq / gamma_a / rowsum
+hipError_t launch_decode_codes(const int8_t* Xq, const float* gamma_a, const int32_t* rowsum, int64_t M,
+                               int64_t K, const uint32_t* packed, int64_t N, const float* gamma, float* Y,
+                               int64_t L, hipStream_t stream);
+
 // a3 + a4 + a6 fused, radix-3 weights
 hipError_t launch_decode_r3(const void* X, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
                             int64_t N, const float* gamma, float* Y, int32_t* acc, int64_t L,

@@ -218,10 +218,11 @@ int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, 
  * (fp32(acc) * fp32(fp32(gamma * gamma_A) / 127)) and A = fp32(r * r), r = max(H, 0).
  *
  * The up projection's epilogue applies ReLU^2, so the hidden layer is written
- * once as float32 and read once by the down projection, whose quantiser reads
- * it as its input.  Decode path (both projections fit the decode kernel): two
- * launches for all L layers.  Prefill path: per layer, quantise X, GEMM with
- * the ReLU^2 epilogue, quantise A, GEMM.
+ * once as float32 and read once by the quantiser of the down projection's
+ * input.  Decode path (both projections fit the decode kernel): three
+ * launches for all L layers (up with the ReLU^2 epilogue, the quantiser over
+ * all L * M hidden rows, down on those codes).  Prefill path: per layer,
+ * quantise X, GEMM with the ReLU^2 epilogue, quantise A, GEMM.
  *
  * X: device [L, M, D] float32 or bfloat16.  packed_up: L matrices of F rows,
  * bitlinear_packed_bytes(F, D) bytes each, back to back; packed_down: L
@@ -230,7 +231,8 @@ int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, 
  * hidden: NULL, or device float32 [L, M, F], 16-byte aligned, receiving A.
  * path: BITLINEAR_PATH_AUTO / _DECODE / _PREFILL as for bitlinear_forward_ex.
  * workspace: >= bitlinear_ffn_workspace_bytes(L, M, D, F), 256-byte aligned
- * (holds A when hidden is NULL, and the prefill path's activation codes).
+ * (holds A when hidden is NULL, and the activation codes: one layer's on the
+ * prefill path, all L layers' hidden rows on the decode path).
  */
 size_t bitlinear_ffn_workspace_bytes(int64_t L, int64_t M, int64_t D, int64_t F);
 

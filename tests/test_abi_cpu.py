@@ -178,7 +178,9 @@ def test_ffn_checks(lib):
     assert call(hid=P(4100)) == abi.ERR_ALIGN
     assert call(M=17, path=1) == abi.ERR_SHAPE            # decode forced beyond 16 tokens
     assert call(ws=None) == abi.ERR_WORKSPACE            # hidden layer needs the workspace
-    assert call(wsb=4 * 128 * 4 - 1) == abi.ERR_WORKSPACE     # decode path: the hidden layer only
+    assert call(wsb=4 * 128 * 4 - 1) == abi.ERR_WORKSPACE     # decode path: the hidden layer ...
+    assert call(wsb=4 * 128 * 4 + 256) == abi.ERR_WORKSPACE   # ... and the codes of its rows
+    assert call(hid=FAKE, ws=None) == abi.ERR_WORKSPACE      # codes even with a caller hidden buffer
     assert call(path=2, wsb=4 * 128 * 4) == abi.ERR_WORKSPACE  # prefill also holds activation codes
     assert call(ws=P(4096 + 16)) == abi.ERR_ALIGN
 
