@@ -483,7 +483,7 @@ def bench_ffn(args, torch, bl, dev):
                "dtype": "i8", "config": cfg,
                "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                            "kernel": "decode_kernel x 2 (up with ReLU^2 epilogue, down), one step"}}
+                            "kernel": "whole block: decode_kernel (up, ReLU^2 epilogue), activation quantiser over all hidden rows, decode_kernel (down, on those codes)"}}
     else:
         out = {"metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "ms_per_step": round(ms_step, 6),
                "dtype": "i8", "config": cfg,
