@@ -60,6 +60,7 @@ FFN_CASES = [
     (3, 300, 170, 90, "bf16", "decode"),
     (8, 2048, 5632, 2048, "bf16", "decode"),
     (16, 100, 3000, 77, "f32", "decode"),
+    (16, 200, 4032, 100, "bf16", "decode"),   # the widest hidden layer the decode path takes at 16 tokens
     (40, 200, 300, 130, "bf16", "prefill"),
     (300, 1000, 650, 333, "f32", "prefill"),
     (5, 513, 260, 64, "bf16", "prefill"),
