@@ -136,8 +136,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
     voff_a = static_cast<uint32_t>(m0 + a_r) * kp32 + 16u * a_c;
     const uint32_t b_n = static_cast<uint32_t>(n0 + b_r);
     b_ok = b_n < N32;
-    b_blk = (b_n & ~15u) * units * 16u;
-    b_j = b_n & 15u;
+    // rows past N: an offset past the resource (2^31 + at most 48), read as zeros
+    b_blk = b_ok ? (b_n & ~15u) * units * 16u : 0x80000000u;
+    b_j = b_ok ? b_n & 15u : 0u;
     b_R = b_ok ? min(16u, N32 - (b_n & ~15u)) : 0u;
     const int64_t m = m0 + tid;
     if (tid < BM && m < M) {
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
     u = u >= units ? u - 1u : u;
     const uint32_t cu = u >> 2;
     const uint32_t W = min(4u, units - 4u * cu);
-    const uint32_t voff_b = b_ok ? b_blk + (cu * b_R * 4u + b_j * W + (u & 3u)) * 16u : 0x80000000u;
+    const uint32_t voff_b = b_blk + (cu * b_R * 4u + b_j * W + (u & 3u)) * 16u;
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q)
       ra[S][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a + k0 - a_adj, q * a_row_step, 0);
