@@ -68,13 +68,13 @@ TRAFFIC = {
     # `bench.py --workload W [--format F] --steps 1 --warmup 1 --no-cpu-baseline`; scale
     # factors 2.0 (FETCH_SIZE) and 1.0 (WRITE_SIZE) from the 1 GiB copy of
     # `bench.py --copy-calibration` (524,303 KiB read, 1,048,576 KiB written).
-    "decode_m1_k2048_n2048": {"sources_sha": "164d4364d6ab4aee", "fetch_bytes": 1078168493, "write_bytes": 8388608},
-    "decode_ffn_up_m8_k2048_n5632": {"sources_sha": "164d4364d6ab4aee", "fetch_bytes": 1088488905, "write_bytes": 67223552},
-    "decode_m1_k2048_n2048/radix3": {"sources_sha": "164d4364d6ab4aee", "fetch_bytes": 1079844094, "write_bytes": 10330112},
-    "decode_m1_k2048_n2048/lut": {"sources_sha": "6d4398590ebb1f5f", "fetch_bytes": 1076015210, "write_bytes": 8388608},
-    "decode_ffn_up_m8_k2048_n5632/lut": {"sources_sha": "6d4398590ebb1f5f", "fetch_bytes": 1082470899, "write_bytes": 67223552},
-    "prefill_ffn_m2048_k4096_n11008": {"sources_sha": "bdac79473c081584", "fetch_bytes": 117091697, "write_bytes": 90275379},
-    "prefill_ffn_m8192_k8192_n28672": {"sources_sha": "bdac79473c081584", "fetch_bytes": 2116616537, "write_bytes": 939611059},
+    "decode_m1_k2048_n2048": {"sources_sha": "164d4364d6ab4aee", "fetch_bytes": 1078168983, "write_bytes": 8388608},
+    "decode_ffn_up_m8_k2048_n5632": {"sources_sha": "164d4364d6ab4aee", "fetch_bytes": 1088488689, "write_bytes": 67223552},
+    "decode_m1_k2048_n2048/radix3": {"sources_sha": "164d4364d6ab4aee", "fetch_bytes": 1079843943, "write_bytes": 10330112},
+    "decode_m1_k2048_n2048/lut": {"sources_sha": "6d4398590ebb1f5f", "fetch_bytes": 1076033620, "write_bytes": 8388608},
+    "decode_ffn_up_m8_k2048_n5632/lut": {"sources_sha": "6d4398590ebb1f5f", "fetch_bytes": 1082515931, "write_bytes": 67223552},
+    "prefill_ffn_m2048_k4096_n11008": {"sources_sha": "cebc415a2a05354b", "fetch_bytes": 117054657, "write_bytes": 90275712},
+    "prefill_ffn_m8192_k8192_n28672": {"sources_sha": "cebc415a2a05354b", "fetch_bytes": 2116002758, "write_bytes": 939598618},
 }
 
 KERNEL_SOURCES = {
