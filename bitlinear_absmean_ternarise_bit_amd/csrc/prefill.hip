@@ -170,9 +170,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_gemm_kernel(
     const uint32_t cu = u >> 2;
     const uint32_t W = min(4u, units - 4u * cu);
     const uint32_t voff_b = b_blk + (cu * b_R * 4u + b_j * W + (u & 3u)) * 16u;
+    // The whole offset, row step included, goes in the lane offset: the
+    // hardware range check covers the lane offset (plus the instruction's
+    // immediate) but not the scalar offset, so only this way does a row past
+    // M land past the resource and read as zeros.
+    const uint32_t a_base = voff_a + k0 - a_adj;
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q)
-      ra[S][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a + k0 - a_adj, q * a_row_step, 0);
+      ra[S][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_base + q * a_row_step, 0, 0);
     if (B_ALL || tid < B_SLOTS)
       rb[S][0] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, 0, 0);
   };
