@@ -18,6 +18,10 @@ int check_mnk(int64_t M, int64_t N, int64_t K) {
   if (K > kMaxK) return BITLINEAR_ERR_SHAPE;
   if (N > (int64_t(1) << 31) || M > (int64_t(1) << 31)) return BITLINEAR_ERR_SHAPE;
   if (static_cast<uint64_t>(N) * static_cast<uint64_t>(K) >= (uint64_t(1) << 32)) return BITLINEAR_ERR_SHAPE;
+  // the kernels address a packed matrix (N * Kp / 4 bytes; the radix-3 form,
+  // N * Kp3 / 5, is never larger) with 32-bit signed byte counts
+  if (static_cast<uint64_t>(N) * static_cast<uint64_t>(padded_k(K)) / 4 >= (uint64_t(1) << 31))
+    return BITLINEAR_ERR_SHAPE;
   if (static_cast<uint64_t>(M) * static_cast<uint64_t>(N) >= (uint64_t(1) << 40)) return BITLINEAR_ERR_SHAPE;
   if (static_cast<uint64_t>(M) * static_cast<uint64_t>(K) >= (uint64_t(1) << 40)) return BITLINEAR_ERR_SHAPE;
   return BITLINEAR_OK;
@@ -39,18 +43,11 @@ bool decode_fits_r3(int64_t M, int64_t K, int64_t N) {
   return M <= kDecodeMaxM && M * (r3_padded_k(K) + 16) <= kDecodeMaxCodes && M * N < (int64_t(1) << 29);
 }
 
-size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
-
 struct PrefillWs {
   int8_t* xq;
   float* ga;
   int32_t* rs;
 };
-
-size_t prefill_ws_bytes(int64_t M, int64_t K) {
-  return align256(static_cast<size_t>(M) * static_cast<size_t>(padded_k(K))) +
-         align256(static_cast<size_t>(M) * 4) + align256(static_cast<size_t>(M) * 4);
-}
 
 PrefillWs prefill_ws(void* ws, int64_t M, int64_t K) {
   char* p = static_cast<char*>(ws);
@@ -69,19 +66,16 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BITLINEAR_OK : BITLINEAR
 
 extern "C" {
 
-int64_t bitlinear_padded_k(int64_t K) { return K < 1 ? 0 : padded_k(K); }
+int64_t bitlinear_padded_k(int64_t K) { return size_args_ok(K) ? padded_k(K) : 0; }
 
 size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
-  if (N < 1 || K < 1) return 0;
-  return static_cast<size_t>(N) * static_cast<size_t>(padded_k(K)) / 4;
+  if (!size_args_ok(N) || !size_args_ok(K)) return 0;
+  return size_mul(static_cast<size_t>(N), static_cast<size_t>(padded_k(K) / 4));
 }
 
 size_t bitlinear_quantize_workspace_bytes(void) { return quantize_workspace_bytes(); }
 
-size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t K) {
-  if (M < 1 || K < 1) return 0;
-  return prefill_ws_bytes(M, K);
-}
+size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t K) { return prefill_ws_bytes(M, K); }
 
 int bitlinear_max_decode_m(void) { return kDecodeMaxM; }
 
@@ -174,13 +168,15 @@ int bitlinear_forward_batched(int64_t L, const void* X, int x_dtype, int64_t M, 
 }
 
 size_t bitlinear_ffn_workspace_bytes(int64_t L, int64_t M, int64_t D, int64_t F) {
-  if (L < 1 || M < 1 || D < 1 || F < 1) return 0;
-  const size_t hidden = align256(static_cast<size_t>(L) * static_cast<size_t>(M) * static_cast<size_t>(F) * 4);
+  if (!size_args_ok(L) || !size_args_ok(M) || !size_args_ok(D) || !size_args_ok(F) ||
+      L > (int64_t(1) << 20) || M > (int64_t(1) << 20))
+    return 0;
+  const size_t hidden = align256(size_mul(size_mul(size_t(L) * size_t(M), size_t(F)), 4));
   // codes of one layer's tokens (prefill path, both projections) or of all
   // layers' hidden rows (decode path)
-  const size_t codes = prefill_ws_bytes(M, D) > prefill_ws_bytes(L * M, F) ? prefill_ws_bytes(M, D)
-                                                                           : prefill_ws_bytes(L * M, F);
-  return hidden + codes;
+  const size_t one = prefill_ws_bytes(M, D), all = prefill_ws_bytes(L * M, F);
+  if (one == 0 || all == 0) return 0;
+  return size_add(hidden, one > all ? one : all);
 }
 
 int bitlinear_ffn_forward(int64_t L, const void* X, int x_dtype, int64_t M, int64_t D, int64_t F,
@@ -250,8 +246,8 @@ int bitlinear_ffn_forward(int64_t L, const void* X, int x_dtype, int64_t M, int6
 }
 
 size_t bitlinear_ste_mask_bytes(int64_t N, int64_t K) {
-  if (N < 1 || K < 1) return 0;
-  return static_cast<size_t>(N) * static_cast<size_t>(mask_words(K)) * 4;
+  if (!size_args_ok(N) || !size_args_ok(K)) return 0;
+  return size_mul(static_cast<size_t>(N), static_cast<size_t>(mask_words(K)) * 4);
 }
 
 int bitlinear_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma, uint32_t* packedT,
@@ -267,7 +263,6 @@ int bitlinear_pack_transposed(const float* W, int64_t N, int64_t K, const float*
 }
 
 size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || N < 1 || K < 1) return 0;
   return backward_workspace_bytes(M, N, K);
 }
 
@@ -295,11 +290,11 @@ int bitlinear_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, cons
                                     static_cast<hipStream_t>(stream)));
 }
 
-int64_t bitlinear_r3_padded_k(int64_t K) { return K < 1 ? 0 : r3_padded_k(K); }
+int64_t bitlinear_r3_padded_k(int64_t K) { return size_args_ok(K) ? r3_padded_k(K) : 0; }
 
 size_t bitlinear_r3_packed_bytes(int64_t N, int64_t K) {
-  if (N < 1 || K < 1) return 0;
-  return static_cast<size_t>(N) * static_cast<size_t>(r3_padded_k(K)) / 5;
+  if (!size_args_ok(N) || !size_args_ok(K)) return 0;
+  return size_mul(static_cast<size_t>(N), static_cast<size_t>(r3_padded_k(K) / 5));
 }
 
 int bitlinear_quantize_weights_r3(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
@@ -357,23 +352,6 @@ int bitlinear_forward_lut(int64_t L, const void* X, int x_dtype, int64_t M, int6
   hipError_t e = launch_act_quant(X, x_dtype, L * M, K, w.xq, w.ga, w.rs, s);
   if (e != hipSuccess) return BITLINEAR_ERR_HIP;
   return hip_status(launch_lut_gemv(w.xq, w.ga, M, K, packed, N, gamma, Y, acc, L, s));
-}
-
-int bitlinear_probe_stream(const void* src, void* dst, int64_t bytes, int blocks, uint32_t* out, void* stream) {
-  if (!src || (!dst && !out)) return BITLINEAR_ERR_NULL;
-  if (blocks < 1 || blocks > (1 << 20) || bytes < 1 || bytes % (int64_t(blocks) * 32768) != 0 ||
-      bytes / blocks >= (int64_t(1) << 31))
-    return BITLINEAR_ERR_SHAPE;
-  if (!aligned(src, 16) || (dst && !aligned(dst, 16)) || (out && !aligned(out, 4))) return BITLINEAR_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(dst ? launch_probe_copy(src, dst, bytes, blocks, s) : launch_probe_read(src, bytes, blocks, out, s));
-}
-
-int bitlinear_probe_mfma_i8(int iters, int blocks, int32_t* out, void* stream) {
-  if (!out) return BITLINEAR_ERR_NULL;
-  if (iters < 1 || blocks < 1 || blocks > (1 << 20)) return BITLINEAR_ERR_SHAPE;
-  if (!aligned(out, 4)) return BITLINEAR_ERR_ALIGN;
-  return hip_status(launch_probe_mfma_i8(iters, blocks, out, static_cast<hipStream_t>(stream)));
 }
 
 const char* bitlinear_status_string(int status) {

@@ -428,15 +428,7 @@ void launch_gemm(const uint16_t* A, int64_t P, int64_t lda, const void* B, int64
                                                               bytes_b, tiles_p, tiles_q);
 }
 
-inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
-
 }  // namespace
-
-size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const int64_t Mp = ((M + 63) / 64) * 64, Np = padded_k(N);
-  return align256(static_cast<size_t>(M * Np * 2)) + align256(static_cast<size_t>(N * Mp * 2)) +
-         align256(static_cast<size_t>(K * Mp * 2));
-}
 
 hipError_t launch_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma, uint32_t* packedT,
                                   uint32_t* mask, hipStream_t stream) {
@@ -451,9 +443,9 @@ hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, 
   const int64_t Mp = ((M + 63) / 64) * 64, Np = padded_k(N), Kp = padded_k(K);
   char* ws = static_cast<char*>(workspace);
   uint16_t* dYp = reinterpret_cast<uint16_t*>(ws);
-  ws += align256(static_cast<size_t>(M * Np * 2));
+  ws += backward_ws_part(M, Np);
   uint16_t* dYt = reinterpret_cast<uint16_t*>(ws);
-  ws += align256(static_cast<size_t>(N * Mp * 2));
+  ws += backward_ws_part(N, Mp);
   uint16_t* At = reinterpret_cast<uint16_t*>(ws);
   if (dX) {
     // dY's rows serve as they are when they start on 16-byte boundaries

@@ -5,21 +5,16 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "sizes.hpp"
 
 namespace bitlinear {
 
-constexpr int kAbsmeanBlocks = 1024;       // fixed grid of the gamma reduction
 constexpr int kDecodeMaxM = 16;            // one MFMA row block of tokens
 constexpr int64_t kDecodeMaxCodes = 65536; // M * Kp int8 codes held in LDS
-
-inline int64_t padded_k(int64_t K) { return ((K + 63) / 64) * 64; }
-// radix-3 rows: a multiple of 80 weights (16 bytes)
-inline int64_t r3_padded_k(int64_t K) { return ((K + 79) / 80) * 80; }
 
 // a1 + a2
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_t* packed,
                                    float* gamma, void* workspace, hipStream_t stream);
-size_t quantize_workspace_bytes();
 // a1 + radix-3 pack (same workspace)
 hipError_t launch_quantize_weights_r3(const float* W, int64_t N, int64_t K, uint8_t* packed,
                                       float* gamma, void* workspace, hipStream_t stream);
@@ -58,18 +53,10 @@ hipError_t launch_lut_gemv(const int8_t* Xq, const float* gamma_a, int64_t M, in
 
 // STE backward: codes of W^T (2-bit format, rows k) and the range mask of W
 // (bits, mask_words(K) 32-bit words per row), then the two bf16 GEMMs
-inline int64_t mask_words(int64_t K) { return (K + 31) / 32; }
 hipError_t launch_pack_transposed(const float* W, int64_t N, int64_t K, const float* gamma, uint32_t* packedT,
                                   uint32_t* mask, hipStream_t stream);
-size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, const uint32_t* packedT,
                            const float* gamma, const int8_t* Xq, const float* gamma_a, const uint32_t* mask,
                            float* dX, float* dW, void* workspace, hipStream_t stream);
-
-// attainable-peak probes (measurement only): a streaming read of `bytes` (one
-// word per thread to `out`), a streaming copy, and back-to-back INT8 MFMAs
-hipError_t launch_probe_read(const void* src, int64_t bytes, int blocks, uint32_t* out, hipStream_t stream);
-hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t stream);
-hipError_t launch_probe_mfma_i8(int iters, int blocks, int32_t* out, hipStream_t stream);
 
 }  // namespace bitlinear

@@ -20,7 +20,7 @@ namespace bitlinear {
 
 namespace {
 
-constexpr int kDigits = 10;
+constexpr int kDigits = kAbsmeanDigits;
 
 struct DigitAcc {
   unsigned long long a0 = 0, a1 = 0, a2 = 0;  // digits T0, T0+1, T0+2
@@ -343,6 +343,5 @@ hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_
   return hipGetLastError();
 }
 
-size_t quantize_workspace_bytes() { return static_cast<size_t>(kAbsmeanBlocks) * kDigits * 8; }
 
 }  // namespace bitlinear

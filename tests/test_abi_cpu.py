@@ -12,6 +12,7 @@ from bitlinear_absmean_ternarise_bit_amd.build import LIB_PATH, build_library
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "bitlinear_probe.h")
 
 P = ctypes.c_void_p
 FAKE = P(4096)  # a non-null, 256-byte aligned address: never dereferenced by these calls
@@ -24,18 +25,32 @@ def lib():
     return abi.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
 
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 27
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(abi.SIGNATURES)
+
+
+def test_probe_library_is_separate(lib):
+    """The attainable-peak probes live in their own library and header: the
+    BitLinear library neither declares nor exports them."""
+    probe = abi.load_probe()
+    names = declared_functions(PROBE_HEADER)
+    assert names == ["bitlinear_probe_mfma_i8", "bitlinear_probe_stream"]
+    for n in names:
+        assert hasattr(probe, n), n
+        assert n not in abi.SIGNATURES
+        with pytest.raises(AttributeError):
+            getattr(lib, n)
+    assert set(names) == set(abi.PROBE_SIGNATURES)
 
 
 def test_sizes(lib):
@@ -201,6 +216,10 @@ def test_quantize_weights_checks(lib):
     assert f(FAKE, 4, -1, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE
     assert f(FAKE, 4, (1 << 20) + 1, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE
     assert f(FAKE, 1 << 13, 1 << 19, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE  # N*K >= 2^32
+    # packed matrices of 2 GiB or more: N * padded_k(K) / 4 >= 2^31 (rows of K = 1 pad to 64)
+    assert f(FAKE, 1 << 28, 1, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE
+    assert f(FAKE, 1 << 27, 1, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE
+    assert f(FAKE, 1 << 27, 64, FAKE, FAKE, FAKE, ws, None) == abi.ERR_SHAPE
     assert f(P(4100), 4, 4, FAKE, FAKE, FAKE, ws, None) == abi.ERR_ALIGN
     assert f(FAKE, 4, 4, P(4104), FAKE, FAKE, ws, None) == abi.ERR_ALIGN
     assert f(FAKE, 4, 4, FAKE, P(4098), FAKE, ws, None) == abi.ERR_ALIGN
@@ -275,7 +294,8 @@ def test_forward_batched_checks(lib):
 
 
 def test_probe_checks(lib):
-    s, m = lib.bitlinear_probe_stream, lib.bitlinear_probe_mfma_i8
+    probe = abi.load_probe()
+    s, m = probe.bitlinear_probe_stream, probe.bitlinear_probe_mfma_i8
     assert s(None, FAKE, 1 << 20, 32, None, None) == abi.ERR_NULL
     assert s(FAKE, None, 1 << 20, 32, None, None) == abi.ERR_NULL       # neither dst nor out
     assert s(FAKE, FAKE, (1 << 20) + 16, 32, None, None) == abi.ERR_SHAPE  # not a multiple of 32 KiB per block
@@ -292,3 +312,46 @@ def test_header_documents_citations_and_conventions():
     for fn in declared_functions():
         assert fn in text
     assert "PMV" in text and "DEVICE pointers" in text
+
+
+def test_size_queries_saturate_to_zero(lib):
+    """Size queries take any int64: out-of-range arguments (< 1 or > 2^40) and
+    products that would not fit in size_t give 0 rather than a wrapped value."""
+    huge, neg = (1 << 63) - 1, -(1 << 63)
+    for v in (0, -1, neg, huge, (1 << 40) + 1):
+        assert lib.bitlinear_padded_k(v) == 0
+        assert lib.bitlinear_r3_padded_k(v) == 0
+        assert lib.bitlinear_packed_bytes(v, 64) == 0 and lib.bitlinear_packed_bytes(64, v) == 0
+        assert lib.bitlinear_r3_packed_bytes(v, 80) == 0 and lib.bitlinear_r3_packed_bytes(80, v) == 0
+        assert lib.bitlinear_forward_workspace_bytes(v, 64) == 0
+        assert lib.bitlinear_forward_workspace_bytes(64, v) == 0
+        assert lib.bitlinear_ste_mask_bytes(v, 64) == 0 and lib.bitlinear_ste_mask_bytes(64, v) == 0
+        assert lib.bitlinear_backward_workspace_bytes(v, 64, 64) == 0
+        assert lib.bitlinear_backward_workspace_bytes(64, v, 64) == 0
+        assert lib.bitlinear_backward_workspace_bytes(64, 64, v) == 0
+        assert lib.bitlinear_ffn_workspace_bytes(v, 8, 64, 64) == 0
+        assert lib.bitlinear_ffn_workspace_bytes(1, v, 64, 64) == 0
+        assert lib.bitlinear_lut_workspace_bytes(v, 8, 64) == 0
+    t = 1 << 40
+    assert lib.bitlinear_padded_k(t) == t
+    assert lib.bitlinear_packed_bytes(t, t) == 0          # 2^78 bytes: does not fit size_t
+    assert lib.bitlinear_backward_workspace_bytes(t, t, t) == 0
+    assert lib.bitlinear_packed_bytes(t, 64) == t * 16
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="a GPU is present: valid arguments would launch kernels on it")
+def test_launch_without_a_device_returns_err_hip(lib):
+    """With no GPU in the machine, calls whose arguments pass every check reach
+    the launch, which fails; the failure comes back as BITLINEAR_ERR_HIP (never
+    an abort).  The pointers are never dereferenced: nothing runs."""
+    ws = lib.bitlinear_quantize_workspace_bytes()
+    assert lib.bitlinear_quantize_weights(FAKE, 4, 4, FAKE, FAKE, FAKE, ws, None) == abi.ERR_HIP
+    assert lib.bitlinear_quantize_activations(FAKE, 1, 2, 8, FAKE, FAKE, FAKE, None) == abi.ERR_HIP
+    # decode path (M <= 16) and prefill path (M > 16) of the forward
+    assert lib.bitlinear_forward(FAKE, 0, 1, 64, FAKE, 16, FAKE, FAKE, None, 0, None) == abi.ERR_HIP
+    wsb = lib.bitlinear_forward_workspace_bytes(64, 128)
+    assert lib.bitlinear_forward(FAKE, 1, 64, 128, FAKE, 32, FAKE, FAKE, FAKE, wsb, None) == abi.ERR_HIP
+    assert lib.bitlinear_forward_batched(4, FAKE, 1, 1, 2048, FAKE, 2048, FAKE, FAKE, None) == abi.ERR_HIP
+    assert lib.bitlinear_forward_quantized(FAKE, FAKE, FAKE, 4, 64, FAKE, 8, FAKE, FAKE, None,
+                                           None) == abi.ERR_HIP
