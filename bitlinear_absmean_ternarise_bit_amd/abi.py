@@ -1,4 +1,6 @@
-"""ctypes view of libbitlinear.so: the C ABI declared in include/bitlinear.h.
+"""ctypes view of libbitlinear.so (the C ABI declared in include/bitlinear.h)
+and of the benchmark's probe library libbitlinear_probe.so
+(include/bitlinear_probe.h).
 
 Loading is lazy and fails loudly: there is no fallback implementation.
 """
@@ -7,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-from .build import LIB_PATH
+from .build import LIB_PATH, PROBE_LIB_PATH
 
 OK = 0
 ERR_NULL = -1
@@ -43,8 +45,6 @@ SIGNATURES = {
     "bitlinear_forward": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _sz, _p]),
     "bitlinear_forward_ex": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _int, _p, _sz, _p]),
     "bitlinear_forward_quantized": (_int, [_p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p]),
-    "bitlinear_probe_stream": (_int, [_p, _p, _i64, _int, _p, _p]),
-    "bitlinear_probe_mfma_i8": (_int, [_int, _int, _p, _p]),
     "bitlinear_forward_batched": (_int, [_i64, _p, _int, _i64, _i64, _p, _i64, _p, _p, _p]),
     "bitlinear_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "bitlinear_ffn_forward": (_int, [_i64, _p, _int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int,
@@ -62,7 +62,14 @@ SIGNATURES = {
     "bitlinear_status_string": (ctypes.c_char_p, [_int]),
 }
 
+# the attainable-peak probes of libbitlinear_probe.so (not the BitLinear ABI)
+PROBE_SIGNATURES = {
+    "bitlinear_probe_stream": (_int, [_p, _p, _i64, _int, _p, _p]),
+    "bitlinear_probe_mfma_i8": (_int, [_int, _int, _p, _p]),
+}
+
 _LIB = None
+_PROBE_LIB = None
 
 
 class BitLinearError(RuntimeError):
@@ -71,14 +78,10 @@ class BitLinearError(RuntimeError):
         super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the HIP library (once).  Raises if it has not been built."""
-    global _LIB
-    if _LIB is not None:
-        return _LIB
+def _open(path: str, signatures) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(
-            f"{path} is missing: build the HIP library first "
+            f"{path} is missing: build the HIP libraries first "
             "(python -m bitlinear_absmean_ternarise_bit_amd.build)")
     # Load torch's HIP runtime first when torch is present: the library then
     # binds to that same runtime, so streams and device pointers from torch are
@@ -88,12 +91,27 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     except ImportError:
         pass
     lib = ctypes.CDLL(path)
-    for name, (res, args) in SIGNATURES.items():
+    for name, (res, args) in signatures.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _LIB = lib
     return lib
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the BitLinear HIP library (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _open(path, SIGNATURES)
+    return _LIB
+
+
+def load_probe(path: str = PROBE_LIB_PATH) -> ctypes.CDLL:
+    """Load the benchmark's probe library (once).  Raises if it has not been built."""
+    global _PROBE_LIB
+    if _PROBE_LIB is None:
+        _PROBE_LIB = _open(path, PROBE_SIGNATURES)
+    return _PROBE_LIB
 
 
 def status_string(status: int) -> str:

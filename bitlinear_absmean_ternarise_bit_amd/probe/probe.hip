@@ -1,6 +1,8 @@
 // Attainable-peak probes: what the chip delivers to plain kernels, reported
-// beside the published peaks (8 TB/s HBM3E, 5 POPS dense INT8).  Not part of
-// the method; the benchmark calls them through the C ABI.
+// beside the published peaks (8 TB/s HBM3E, 5 POPS dense INT8).  They are a
+// measurement aid of the benchmark, built into their own library with their
+// own header (include/bitlinear_probe.h); they are not part of the BitLinear
+// library or its ABI.
 //
 //  - stream_read_kernel: every lane reads 16-byte vectors with the streaming
 //    (nontemporal) cache policy, in batches of eight per lane, each batch one
@@ -9,11 +11,18 @@
 //    destination;
 //  - mfma_i8_kernel: every wave issues v_mfma_i32_32x32x32_i8 back to back on
 //    eight independent accumulators (no memory traffic inside the loop).
-#include "kernels.hpp"
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bitlinear_probe.h"
 
 namespace bitlinear {
 
 namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kStreamnt = 2;  // cache-policy bits of a buffer access: streaming
 
@@ -80,20 +89,37 @@ __global__ __launch_bounds__(256, 2) void mfma_i8_kernel(int iters, int32_t* __r
 
 }  // namespace
 
-hipError_t launch_probe_read(const void* src, int64_t bytes, int blocks, uint32_t* out, hipStream_t stream) {
-  stream_read_kernel<<<blocks, 256, 0, stream>>>(static_cast<const uint32_t*>(src), bytes / blocks, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t stream) {
-  stream_copy_kernel<<<blocks, 256, 0, stream>>>(static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst),
-                                                 bytes / blocks);
-  return hipGetLastError();
-}
-
-hipError_t launch_probe_mfma_i8(int iters, int blocks, int32_t* out, hipStream_t stream) {
-  mfma_i8_kernel<<<blocks, 256, 0, stream>>>(iters, out);
-  return hipGetLastError();
-}
-
 }  // namespace bitlinear
+
+namespace {
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int hip_status(hipError_t e) { return e == hipSuccess ? BITLINEAR_PROBE_OK : BITLINEAR_PROBE_ERR_HIP; }
+}  // namespace
+
+extern "C" {
+
+int bitlinear_probe_stream(const void* src, void* dst, int64_t bytes, int blocks, uint32_t* out, void* stream) {
+  if (!src || (!dst && !out)) return BITLINEAR_PROBE_ERR_NULL;
+  if (blocks < 1 || blocks > (1 << 20) || bytes < 1 || bytes % (int64_t(blocks) * 32768) != 0 ||
+      bytes / blocks >= (int64_t(1) << 31))
+    return BITLINEAR_PROBE_ERR_SHAPE;
+  if (!aligned(src, 16) || (dst && !aligned(dst, 16)) || (out && !aligned(out, 4))) return BITLINEAR_PROBE_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t per_block = bytes / blocks;
+  if (dst)
+    bitlinear::stream_copy_kernel<<<blocks, 256, 0, s>>>(static_cast<const uint32_t*>(src),
+                                                         static_cast<uint32_t*>(dst), per_block);
+  else
+    bitlinear::stream_read_kernel<<<blocks, 256, 0, s>>>(static_cast<const uint32_t*>(src), per_block, out);
+  return hip_status(hipGetLastError());
+}
+
+int bitlinear_probe_mfma_i8(int iters, int blocks, int32_t* out, void* stream) {
+  if (!out) return BITLINEAR_PROBE_ERR_NULL;
+  if (iters < 1 || blocks < 1 || blocks > (1 << 20)) return BITLINEAR_PROBE_ERR_SHAPE;
+  if (!aligned(out, 4)) return BITLINEAR_PROBE_ERR_ALIGN;
+  bitlinear::mfma_i8_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, out);
+  return hip_status(hipGetLastError());
+}
+
+}  // extern "C"

@@ -1,4 +1,4 @@
-"""The attainable-peak probes (measurement hooks of the C ABI) touch exactly
+"""The attainable-peak probes (the benchmark's libbitlinear_probe.so) touch exactly
 the bytes they are timed on: the streaming read folds every word of its slice
 (checked against a host emulation of the access pattern), the copy
 reproduces its source, and the MFMA loop is deterministic."""
@@ -23,7 +23,7 @@ def test_probe_stream_read_folds_every_word():
     host = rng.integers(0, 2 ** 32, size=blocks * per_block // 4, dtype=np.uint64).astype(np.uint32)
     src = torch.from_numpy(host.view(np.int32)).to(DEV)
     out = torch.zeros(blocks * 256, dtype=torch.int32, device=DEV)
-    lib = bl.abi.load()
+    lib = bl.abi.load_probe()
     bl.abi.check("probe", lib.bitlinear_probe_stream(src.data_ptr(), None, blocks * per_block, blocks,
                                                       out.data_ptr(), stream()))
     torch.cuda.synchronize()
@@ -38,14 +38,14 @@ def test_probe_stream_copy():
     n = 4 * 32768 * 5
     src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device=DEV)
     dst = torch.zeros_like(src)
-    lib = bl.abi.load()
+    lib = bl.abi.load_probe()
     bl.abi.check("probe", lib.bitlinear_probe_stream(src.data_ptr(), dst.data_ptr(), n, 5, None, stream()))
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
 
 
 def test_probe_mfma_deterministic():
-    lib = bl.abi.load()
+    lib = bl.abi.load_probe()
     a = torch.empty(4 * 256, dtype=torch.int32, device=DEV)
     b = torch.empty_like(a)
     bl.abi.check("probe", lib.bitlinear_probe_mfma_i8(7, 4, a.data_ptr(), stream()))
