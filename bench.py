@@ -27,6 +27,13 @@ of the 7B-like projection in bf16 TFLOP/s.
 the prefill forward instead (activation quantiser + INT8-MFMA GEMM) and
 reports INT8 TOPS (2*M*N*K per step) against the 5.0 POPS dense INT8 peak.
 
+The default line carries both halves of the metric: after the decode step it
+holds a "prefill" object with one entry per prefill workload (8192x8192x28672
+and 2048x4096x11008): the whole prefill forward (activation quantiser +
+INT8-MFMA GEMM) in INT8 TOPS, the GEMM alone ("kernel_ms") with its roofline
+against the dense INT8 peak, and the CPU oracle beside it (--no-prefill leaves
+them out).
+
 Weight quantisation (absmean + ternarise + pack) runs once per weight matrix
 before the timed region; it is timed separately and reported under
 "weight_quantisation".
@@ -329,13 +336,14 @@ def cpu_naive_loop(P, q, seconds=3.0):
 # prefill
 # ---------------------------------------------------------------------------
 
-def bench_prefill(args, torch, bl, dev):
+def bench_prefill(args, torch, bl, dev, workload=None):
     import numpy as np
     from bitlinear_absmean_ternarise_bit_amd.workloads import make_workload
 
-    P = make_workload(args.workload)
+    workload = workload or args.workload
+    P = make_workload(workload)
     M, K, N = P.M, P.K, P.N
-    log(f"[bench] prefill {args.workload}: M={M} K={K} N={N}")
+    log(f"[bench] prefill {workload}: M={M} K={K} N={N}")
     W = torch.from_numpy(P.W).to(dev)
     packed, gamma = bl.quantize_weights(W)  # first call loads the kernels: not timed
     ws_q = torch.empty((bl.abi.load().bitlinear_quantize_workspace_bytes(),), dtype=torch.uint8, device=dev)
@@ -373,19 +381,39 @@ def bench_prefill(args, torch, bl, dev):
         "metric": METRIC, "value": round(tops, 2), "unit": "TOPS",
         "ms_per_step": round(ms_step, 6),
         "dtype": "i8",
-        "config": {"workload": args.workload, "M": M, "K": K, "N": N, "x_dtype": "bf16",
+        "config": {"workload": workload, "M": M, "K": K, "N": N, "x_dtype": "bf16",
                    "ops_per_step": ops, "bytes_per_step": step_bytes},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": traffic_for(args.workload, "prefill"),
+                     "traffic": traffic_for(workload, "prefill"),
                      "kernel": "prefill_gemm_kernel (INT8 MFMA + fused rescale)",
                      "kernel_ms": round(gemm_ms, 6)},
         "weight_quantisation": {"ms_per_matrix": round(tq.ms, 4),
                                 "GBps": round((4 * N * K + N * bl.packed_words(K) * 4) / (tq.ms * 1e-3) / 1e9, 2),
                                 "note": "absmean + ternarise + pack, offline, not in the step"},
     }
+    del X, Y, ws, Xq, ga, rs, packed
+    torch.cuda.empty_cache()
     if args.cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_prefill(P, args.cpu_seconds)
+    return out
+
+
+def prefill_objects(args, torch, bl, dev) -> dict:
+    """The prefill half of the metric, carried in the default (decode) line:
+    for each prefill workload, the whole forward (quantiser + GEMM) in TOPS,
+    the GEMM alone (kernel_ms) with its roofline against the INT8 peak, and
+    the CPU oracle beside it."""
+    out = {}
+    for w in PREFILL_WORKLOADS[::-1]:  # the largest first
+        o = bench_prefill(args, torch, bl, dev, workload=w)
+        cfg = o.pop("config")
+        o.pop("metric")
+        o = {"workload": w, "M": cfg["M"], "K": cfg["K"], "N": cfg["N"], "x_dtype": cfg["x_dtype"],
+             "ops_per_step": cfg["ops_per_step"], "steps": args.steps, **o}
+        if "cpu_baseline" in o:
+            o["cpu_baseline"].update(host_cpu())
+        out[w] = o
     return out
 
 
@@ -610,7 +638,7 @@ def attainable_peaks(torch, bl, dev, read_blocks: int = 2048, mfma_iters: int = 
     a 1 GiB streaming read (16-byte nontemporal loads, one contiguous slice per
     workgroup), a 512 MiB -> 512 MiB streaming copy, and back-to-back INT8
     MFMAs on registers (two workgroups per CU)."""
-    lib = bl.abi.load()
+    lib = bl.abi.load_probe()
     stream = torch.cuda.current_stream(dev).cuda_stream
     nbytes = 1 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
@@ -646,6 +674,15 @@ def attainable_peaks(torch, bl, dev, read_blocks: int = 2048, mfma_iters: int = 
 
 
 def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        res = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for ln in res.stdout.splitlines():
+            if ln.startswith("Model name:"):
+                return ln.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for ln in f:
@@ -654,6 +691,16 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def host_cpu() -> dict:
+    """What the CPU baseline ran on: the model, the logical CPUs the host
+    offers (nproc) and those this process may use."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": cpu_model(), "nproc": os.cpu_count() or 1, "cpus_usable": usable}
 
 
 def copy_calibration(torch, dev):
@@ -682,6 +729,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-prefill", dest="prefill", action="store_false",
+                    help="decode workloads: leave out the prefill objects (both prefill workloads, "
+                         "timed after the decode step) from the line")
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip the attainable-peak probes (streaming read and copy, register MFMAs)")
     args = ap.parse_args()
@@ -718,7 +768,9 @@ def main():
             "config": out.pop("config")}
     line.update(out)
     if "cpu_baseline" in line:
-        line["cpu_baseline"]["cpu_model"] = cpu_model()
+        line["cpu_baseline"].update(host_cpu())
+    if args.prefill and args.workload in DECODE_WORKLOADS and args.format == "2bit":
+        line["prefill"] = prefill_objects(args, torch, bl, dev)
     if args.peaks:
         line["attainable"] = attainable_peaks(torch, bl, dev)
     props = torch.cuda.get_device_properties(dev)
