@@ -23,6 +23,7 @@ __all__ = [
     "forward",
     "forward_batched",
     "forward_quantized",
+    "forward_noalloc",
     "max_decode_m",
     "decode_fits",
     "ffn_forward",
@@ -180,6 +181,35 @@ def forward(X, packed, gamma, K: int | None = None, path: str = "auto", return_a
                                        _ptr(Y), _ptr(acc), _PATHS[path], _ptr(ws), ws_bytes,
                                        _stream(X)))
     return (Y, acc) if return_acc else Y
+
+
+def forward_noalloc(X, packed, gamma, K: int | None = None, out=None):
+    """bitlinear_forward_noalloc: the same forward with the library's own
+    per-GPU scratch array as the prefill workspace (the C call allocates
+    nothing; pass ``out`` to allocate nothing here either).  Calls that overlap
+    on one GPU share that array and must be serialised."""
+    torch = _torch()
+    _require_cuda(X, "X")
+    _require_cuda(packed, "packed")
+    _require_cuda(gamma, "gamma")
+    if X.dim() != 2 or packed.dim() != 2:
+        raise ValueError("X must be [M, K] and packed [N, words]")
+    M, Kx = X.shape
+    K = Kx if K is None else K
+    if K != Kx:
+        raise ValueError("K does not match X")
+    N = packed.shape[0]
+    if packed.shape[1] != packed_words(K) or packed.element_size() != 4:
+        raise ValueError("packed does not hold padded_k(K) // 16 32-bit words per row")
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=X.device)
+    if Y.shape != (M, N) or Y.dtype != torch.float32:
+        raise ValueError("out must be float32 [M, N]")
+    _require_cuda(Y, "out")
+    lib = abi.load()
+    abi.check("bitlinear_forward_noalloc",
+              lib.bitlinear_forward_noalloc(_ptr(X), _x_dtype(X), M, K, _ptr(packed), N, _ptr(gamma),
+                                            _ptr(Y), _stream(X)))
+    return Y
 
 
 def forward_quantized(Xq, gamma_a, rowsum, packed, gamma, K: int, return_acc: bool = False, out=None):

@@ -59,8 +59,11 @@ SIGNATURES = {
     "bitlinear_forward_r3": (_int, [_i64, _p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _p]),
     "bitlinear_lut_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bitlinear_forward_lut": (_int, [_i64, _p, _int, _i64, _i64, _p, _i64, _p, _p, _p, _p, _sz, _p]),
+    "bitlinear_forward_noalloc": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p, _p]),
     "bitlinear_status_string": (ctypes.c_char_p, [_int]),
 }
+
+NOALLOC_SCRATCH_BYTES = 80 * 1024 * 1024  # BITLINEAR_NOALLOC_SCRATCH_BYTES
 
 # the attainable-peak probes of libbitlinear_probe.so (not the BitLinear ABI)
 PROBE_SIGNATURES = {

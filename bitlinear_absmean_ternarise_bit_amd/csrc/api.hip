@@ -64,6 +64,27 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BITLINEAR_OK : BITLINEAR
 
 }  // namespace
 
+namespace bitlinear {
+
+int check_forward_args(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed, int64_t N,
+                       const float* gamma, const float* Y, const int32_t* acc, int path, bool* decode) {
+  if (!X || !packed || !gamma || !Y) return BITLINEAR_ERR_NULL;
+  int st = check_mnk(M, N, K);
+  if (st) return st;
+  st = check_x(X, x_dtype);
+  if (st) return st;
+  if (path != BITLINEAR_PATH_AUTO && path != BITLINEAR_PATH_DECODE && path != BITLINEAR_PATH_PREFILL)
+    return BITLINEAR_ERR_ARG;
+  if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(Y, 4) || (acc && !aligned(acc, 4)))
+    return BITLINEAR_ERR_ALIGN;
+  const bool fits = decode_fits(M, K, N);
+  if (path == BITLINEAR_PATH_DECODE && !fits) return BITLINEAR_ERR_SHAPE;
+  *decode = path == BITLINEAR_PATH_DECODE || (path == BITLINEAR_PATH_AUTO && fits);
+  return BITLINEAR_OK;
+}
+
+}  // namespace bitlinear
+
 extern "C" {
 
 int64_t bitlinear_padded_k(int64_t K) { return size_args_ok(K) ? padded_k(K) : 0; }
@@ -108,18 +129,9 @@ int bitlinear_quantize_activations(const void* X, int x_dtype, int64_t M, int64_
 int bitlinear_forward_ex(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
                          int64_t N, const float* gamma, float* Y, int32_t* acc, int path,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  if (!X || !packed || !gamma || !Y) return BITLINEAR_ERR_NULL;
-  int st = check_mnk(M, N, K);
+  bool decode = false;
+  const int st = bitlinear::check_forward_args(X, x_dtype, M, K, packed, N, gamma, Y, acc, path, &decode);
   if (st) return st;
-  st = check_x(X, x_dtype);
-  if (st) return st;
-  if (path != BITLINEAR_PATH_AUTO && path != BITLINEAR_PATH_DECODE && path != BITLINEAR_PATH_PREFILL)
-    return BITLINEAR_ERR_ARG;
-  if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(Y, 4) || (acc && !aligned(acc, 4)))
-    return BITLINEAR_ERR_ALIGN;
-  const bool fits = decode_fits(M, K, N);
-  if (path == BITLINEAR_PATH_DECODE && !fits) return BITLINEAR_ERR_SHAPE;
-  const bool decode = path == BITLINEAR_PATH_DECODE || (path == BITLINEAR_PATH_AUTO && fits);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (decode) return hip_status(launch_decode(X, x_dtype, M, K, packed, N, gamma, Y, acc, 1, s));
   if (!workspace || workspace_bytes < prefill_ws_bytes(M, K)) return BITLINEAR_ERR_WORKSPACE;

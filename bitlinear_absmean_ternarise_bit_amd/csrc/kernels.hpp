@@ -12,6 +12,12 @@ namespace bitlinear {
 constexpr int kDecodeMaxM = 16;            // one MFMA row block of tokens
 constexpr int64_t kDecodeMaxCodes = 65536; // M * Kp int8 codes held in LDS
 
+// The forward's argument checks (null pointers, sizes, dtype, path,
+// alignment): a BITLINEAR_* status, and in *decode whether the decode path
+// runs.  Shared by the forward entry points (api.hip, noalloc.hip).
+int check_forward_args(const void* X, int x_dtype, int64_t M, int64_t K, const uint32_t* packed, int64_t N,
+                       const float* gamma, const float* Y, const int32_t* acc, int path, bool* decode);
+
 // a1 + a2
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, uint32_t* packed,
                                    float* gamma, void* workspace, hipStream_t stream);

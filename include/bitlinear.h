@@ -376,6 +376,35 @@ int bitlinear_forward_lut(int64_t L, const void* X, int x_dtype, int64_t M, int6
                           float* Y, int32_t* acc, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* ---- the forward without allocation ------------------------------------ */
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, hosts that forbid allocation.  The same
+ * forward as bitlinear_forward (same kernels, same results, bit for bit),
+ * without a workspace argument: the prefill path's activation codes, scales
+ * and code sums go to a scratch array that the library holds on every GPU it
+ * runs on (BITLINEAR_NOALLOC_SCRATCH_BYTES of device memory per GPU, from the
+ * moment the library's code is loaded on that GPU until the process ends).
+ * The call itself allocates nothing.
+ *
+ * Limit: the prefill path (M > bitlinear_max_decode_m(), or rows too long for
+ * the decode kernel) needs bitlinear_forward_workspace_bytes(M, K) <=
+ * BITLINEAR_NOALLOC_SCRATCH_BYTES (80 MiB: e.g. 8192 tokens of K = 8192, or
+ * 16384 tokens of K = 4096), else the call returns BITLINEAR_ERR_WORKSPACE and
+ * enqueues nothing.  The decode path uses no scratch.
+ *
+ * Every call on one GPU shares that GPU's scratch array: calls that may
+ * overlap on one GPU (different streams, or host threads without an order
+ * between them) race and give wrong results; serialise them.  The array is
+ * looked up once per GPU, on the first call that runs there.
+ * Arguments, errors and the stream's role are as for bitlinear_forward.
+ */
+#define BITLINEAR_NOALLOC_SCRATCH_BYTES (80u * 1024u * 1024u)
+
+int bitlinear_forward_noalloc(const void* X, int x_dtype, int64_t M, int64_t K,
+                              const uint32_t* packed, int64_t N, const float* gamma,
+                              float* Y, void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* bitlinear_status_string(int status);
 

@@ -33,7 +33,7 @@ def declared_functions(header=HEADER):
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(abi.SIGNATURES)
@@ -355,3 +355,24 @@ def test_launch_without_a_device_returns_err_hip(lib):
     assert lib.bitlinear_forward_batched(4, FAKE, 1, 1, 2048, FAKE, 2048, FAKE, FAKE, None) == abi.ERR_HIP
     assert lib.bitlinear_forward_quantized(FAKE, FAKE, FAKE, 4, 64, FAKE, 8, FAKE, FAKE, None,
                                            None) == abi.ERR_HIP
+
+
+def test_forward_noalloc_checks(lib):
+    """The allocation-free forward checks its arguments like the forward, and
+    rejects a prefill problem whose workspace exceeds its scratch array before
+    any HIP call."""
+    f = lib.bitlinear_forward_noalloc
+    assert f(None, 0, 64, 128, FAKE, 32, FAKE, FAKE, None) == abi.ERR_NULL
+    assert f(FAKE, 0, 64, 128, FAKE, 32, FAKE, None, None) == abi.ERR_NULL
+    assert f(FAKE, 0, 0, 128, FAKE, 32, FAKE, FAKE, None) == abi.ERR_SHAPE
+    assert f(FAKE, 0, 1, 1, FAKE, 1 << 28, FAKE, FAKE, None) == abi.ERR_SHAPE
+    assert f(FAKE, 4, 64, 128, FAKE, 32, FAKE, FAKE, None) == abi.ERR_DTYPE
+    assert f(FAKE, 0, 64, 128, P(4104), 32, FAKE, FAKE, None) == abi.ERR_ALIGN
+    # 16384 tokens of K = 8192: 128 MiB of codes, more than the 80 MiB array
+    assert lib.bitlinear_forward_workspace_bytes(16384, 8192) > abi.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, 1, 16384, 8192, FAKE, 64, FAKE, FAKE, None) == abi.ERR_WORKSPACE
+    # the largest problems of the two prefill workloads fit
+    assert lib.bitlinear_forward_workspace_bytes(8192, 8192) <= abi.NOALLOC_SCRATCH_BYTES
+    assert lib.bitlinear_forward_workspace_bytes(16384, 4096) <= abi.NOALLOC_SCRATCH_BYTES
+    m = re.search(r"#define BITLINEAR_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", open(HEADER).read())
+    assert m and int(m.group(1)) << 20 == abi.NOALLOC_SCRATCH_BYTES
