@@ -39,6 +39,8 @@
 //            multiply, one mask and half a byte permute give four codes.  The
 //            twenty code dwords of a unit, in (word, digit) order, are k = 4f
 //            .. 4f+3 of the unit: five B operands for five MFMAs.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "quant_act.hpp"
 
@@ -122,7 +124,12 @@ __host__ __device__ inline int stage_bytes(int M, int groups, bool with_acc, int
 // DT: 0 = float32 tokens, 1 = bfloat16 tokens, both quantised in phase A;
 // 2 = int8 codes [L, M, Kp] quantised beforehand, with gamma_A and the code
 // sums in ga_in / rs_in [L, M] (phase A only copies them into LDS).
-template <int FMT, int DT, bool VEC, int EPI>
+// SPLIT: for calls with too few weight rows to give every CU a workgroup (a
+// single layer, token by token): a workgroup owns one block of 16 weight
+// rows and its four waves each walk a quarter of the rows' load chunks; the
+// exact INT32 partial sums are added in LDS (in any order: they are
+// integers) and one wave rescales and stores them.
+template <int FMT, int DT, bool VEC, int EPI, bool SPLIT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const void* __restrict__ X, int M, int64_t K, int64_t Kp, int64_t units,
     const uint32_t* __restrict__ packed, int64_t N, const float* __restrict__ gamma,
@@ -145,7 +152,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const int64_t layer = v / blocks_per_layer;
   const int rb = static_cast<int>(v - layer * blocks_per_layer);
   const int64_t lds_stride = Kp + 16;  // +16 bytes: token rows start on different banks
-  const int stage = stage_bytes(M, groups, EPI == kEpiAcc, M * lds_stride);  // per wave, 0: direct stores
+  // per wave, 0: direct stores (always in the SPLIT form)
+  const int stage = SPLIT ? 0 : stage_bytes(M, groups, EPI == kEpiAcc, M * lds_stride);
   X = static_cast<const char*>(X) + layer * M * (DT == 2 ? Kp : K * esize);
   packed += layer * N * units * 4;
   Y += layer * M * N;
@@ -156,9 +164,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int j = lane & 15;
   const int g = lane >> 4;
-  const int64_t n_base = (static_cast<int64_t>(rb) * kWaves + wave) * groups * kRowsPerWave;
+  const int64_t n_base = SPLIT ? static_cast<int64_t>(rb) * kRowsPerWave
+                               : (static_cast<int64_t>(rb) * kWaves + wave) * groups * kRowsPerWave;
   const int chunks = static_cast<int>((units + 3) >> 2);  // load instructions per row
-  const int bpg = (chunks + kUnroll - 1) / kUnroll;       // batches per row group
+  // the wave's load chunks of a row: all of them, or (SPLIT) its quarter
+  const int c_lo = SPLIT ? wave * chunks / kWaves : 0;
+  const int c_hi = SPLIT ? (wave + 1) * chunks / kWaves : chunks;
+  const int bpg = (c_hi - c_lo + kUnroll - 1) / kUnroll;  // batches per row group
   const int nbatch = groups * bpg;
 
   // Packed rows are read, and outputs written, through buffer resources over
@@ -191,10 +203,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const bool row_ok = valid && static_cast<uint32_t>(j) < R;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t cs = static_cast<uint32_t>(cb * kUnroll + u);
+      const uint32_t cs = static_cast<uint32_t>(c_lo + cb * kUnroll + u);
       const uint32_t un = cs * 4u + g;
       const uint32_t W = min(4u, units32 - min(units32, 4u * cs));  // units of chunk cs
-      const uint32_t off = (row_ok && un < units32) ? blk + (cs * R * 4u + j * W + g) * 16u : kOff;
+      const bool ok = row_ok && un < units32 && (!SPLIT || cs < static_cast<uint32_t>(c_hi));
+      const uint32_t off = ok ? blk + (cs * R * 4u + j * W + g) * 16u : kOff;
       const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off, 0, kNontemporal);
       r[u] = make_uint4(v[0], v[1], v[2], v[3]);
     }
@@ -262,7 +275,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const int cb = b - (b / bpg) * bpg;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t un = static_cast<uint32_t>(cb * kUnroll + u) * 4u + g;
+      const int cs = c_lo + cb * kUnroll + u;
+      if (SPLIT && cs >= c_hi) continue;  // past the wave's quarter (wave-uniform)
+      const uint32_t un = static_cast<uint32_t>(cs) * 4u + g;
       // units past the row end give all-zero operands, so any in-bounds
       // activation codes may pair with them
       const uint32_t abase = un < units32 ? kPerUnit * un : 0u;
@@ -287,6 +302,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   // the accumulator waits for the group's chain of MFMAs; the caller issues
   // the next loads first, so two batches stay in flight meanwhile.
   auto epilogue = [&](int b) {
+    if constexpr (SPLIT) return;  // once, after the waves' partial sums are added
     const int gi = b / bpg;
     if (b - gi * bpg != bpg - 1) return;
     const int x = gi * kRowsPerWave + j;
@@ -335,6 +351,31 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     mfma_batch(b, buf0);
     epilogue(b);
   }
+  if constexpr (SPLIT) {
+    // add the four waves' partial sums of the block's 16 rows, then rescale
+    // and store them from wave 0 (lane holds tokens 4g + r of row j)
+    v4i* red = reinterpret_cast<v4i*>(sxq + M * lds_stride);
+    red[threadIdx.x] = c;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) c += red[w * kWave + lane];
+      const uint32_t n = static_cast<uint32_t>(n_base + j);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;
+        const int v = c[r] - tok_rs[r];
+        float y = __fmul_rn(static_cast<float>(v), tok_scale[r]);
+        if constexpr (EPI == kEpiRelu2) {
+          const float rl = fmaxf(y, 0.0f);
+          y = __fmul_rn(rl, rl) + 0.0f;  // + 0: no negative zero
+        }
+        const uint32_t off = (i < M && n < N32) ? (static_cast<uint32_t>(i) * N32 + n) * 4u : kOff;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), ysrc, off, 0, 0);
+        if constexpr (EPI == kEpiAcc) __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(v), asrc, off, 0, 0);
+      }
+    }
+  }
   if (stage) {
     // the wave's outputs, row-contiguous per token; LDS operations of one
     // wave complete in order, so the staged values are visible here
@@ -364,6 +405,11 @@ int pick_groups(int64_t L, int64_t N) {
   return 1;
 }
 
+// Calls whose normal grid would leave most CUs without a workgroup (a
+// single layer of a few thousand rows, say) take the SPLIT form instead: one
+// 16-row block per workgroup, K split over its waves.
+constexpr int64_t kSplitBelow = 256;
+
 template <int FMT, int DT, bool VEC>
 hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed, int64_t N,
                     const float* gamma, float* Y, int32_t* acc, int64_t L, bool relu2,
@@ -372,27 +418,37 @@ hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed,
   const int64_t units = Kp / Format<FMT>::kPerUnit;
   const int groups = pick_groups(L, N);
   const int64_t rows = int64_t(kWaves) * kRowsPerWave * groups;
-  const int bpl = static_cast<int>((N + rows - 1) / rows);
+  const int64_t blocks16 = (N + kRowsPerWave - 1) / kRowsPerWave;  // 16-row blocks per layer
+  int bpl = static_cast<int>((N + rows - 1) / rows);
+  const bool split = L * bpl < kSplitBelow && blocks16 > bpl;
+  if (split) bpl = static_cast<int>(blocks16);
   const unsigned blocks = static_cast<unsigned>(L * bpl);
   const int m = static_cast<int>(M);
   const bool with_acc = acc != nullptr && !relu2;
   const int64_t code_bytes = M * (Kp + 16);
+  // after the codes: the waves' staged outputs, or (SPLIT) their partial sums
   const size_t lds = static_cast<size_t>(code_bytes) +
-                     static_cast<size_t>(kWaves) * stage_bytes(m, groups, with_acc, code_bytes);
-  if constexpr (DT == 2) {
-    decode_kernel<FMT, DT, VEC, kEpiY><<<blocks, kDecodeThreads, lds, stream>>>(
-        X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, ga_in, rs_in);
-  } else {
-    if (FMT == 2 && relu2)
-      decode_kernel<FMT, DT, VEC, FMT == 2 ? kEpiRelu2 : kEpiY><<<blocks, kDecodeThreads, lds, stream>>>(
-          X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, nullptr, nullptr);
-    else if (acc)
-      decode_kernel<FMT, DT, VEC, kEpiAcc><<<blocks, kDecodeThreads, lds, stream>>>(
-          X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, nullptr, nullptr);
-    else
-      decode_kernel<FMT, DT, VEC, kEpiY><<<blocks, kDecodeThreads, lds, stream>>>(
-          X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, nullptr, nullptr);
-  }
+                     (split ? static_cast<size_t>(kDecodeThreads) * sizeof(v4i)
+                            : static_cast<size_t>(kWaves) * stage_bytes(m, groups, with_acc, code_bytes));
+  auto go = [&](auto split_tag) {
+    constexpr bool S = decltype(split_tag)::value;
+    if constexpr (DT == 2) {
+      decode_kernel<FMT, DT, VEC, kEpiY, S><<<blocks, kDecodeThreads, lds, stream>>>(
+          X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, ga_in, rs_in);
+    } else {
+      if (FMT == 2 && relu2)
+        decode_kernel<FMT, DT, VEC, FMT == 2 ? kEpiRelu2 : kEpiY, S><<<blocks, kDecodeThreads, lds, stream>>>(
+            X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, nullptr, nullptr);
+      else if (acc)
+        decode_kernel<FMT, DT, VEC, kEpiAcc, S><<<blocks, kDecodeThreads, lds, stream>>>(
+            X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, nullptr, nullptr);
+      else
+        decode_kernel<FMT, DT, VEC, kEpiY, S><<<blocks, kDecodeThreads, lds, stream>>>(
+            X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, nullptr, nullptr);
+    }
+  };
+  if (split) go(std::true_type());
+  else go(std::false_type());
   return hipGetLastError();
 }
 

@@ -1,0 +1,104 @@
+"""The decode kernel's two launch forms give the same bits.
+
+A call with few weight rows (a single layer: 2048 rows are 32 workgroups of
+the normal form) takes the split form: one 16-row block per workgroup, the
+row's K split over its four waves and the exact INT32 partial sums added in
+LDS.  The same layers inside a batch of several hundred take the normal
+form (each wave walks whole rows).  Both forms must agree bit for bit
+(integer sums are order-free, the rescale is the same), and the split form
+must match the oracle, for both weight formats and all three epilogues.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bitlinear_absmean_ternarise_bit_amd as bl
+import oracle as O
+from bitlinear_absmean_ternarise_bit_amd.workloads import random_problem
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check_y(y, yr):
+    y = np.asarray(y, dtype=np.float64)
+    yr = np.asarray(yr, dtype=np.float64)
+    assert np.all(np.abs(y - yr) <= 1e-5 * np.abs(yr))
+
+
+def pool(L, M, K, N, seed, fmt="2bit"):
+    """L layers: layer 0 from a seeded numpy problem (checked against the
+    oracle), the others from torch's seeded device generator."""
+    P = random_problem(M, K, N, seed=seed, x_dtype="bf16")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    X = (torch.randn((L, M, K), generator=g, device=DEV) * 2.0).to(torch.bfloat16)
+    X[0].copy_(torch.from_numpy(P.X_bf16_bits.view(np.int16)).view(torch.bfloat16))
+    W = torch.randn((N, K), generator=g, device=DEV) * 0.02
+    if fmt == "radix3":
+        packed = torch.empty((L, N, bl.r3_row_bytes(K)), dtype=torch.uint8, device=DEV)
+        quant = bl.quantize_weights_r3
+    else:
+        packed = torch.empty((L, N, bl.packed_words(K)), dtype=torch.int32, device=DEV)
+        quant = bl.quantize_weights
+    gamma = torch.empty((L,), dtype=torch.float32, device=DEV)
+    for l in range(L):
+        Wl = torch.from_numpy(P.W).to(DEV) if l == 0 else W * (1.0 + 0.01 * l)
+        quant(Wl, out_packed=packed[l], out_gamma=gamma[l:l + 1])
+    return P, X, packed, gamma
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 2048, 2048), (8, 2048, 5632), (3, 1000, 200), (16, 4000, 129),
+                                   (1, 65472, 64), (5, 9, 40)])
+def test_split_form_equals_streaming_form(M, K, N):
+    L = max(300, -(-2048 // max(1, (N + 63) // 64)))  # enough row blocks for the normal form
+    say(f"decode split vs streaming M={M} K={K} N={N} (batch of {L})")
+    P, X, packed, gamma = pool(L, M, K, N, seed=M + K + N)
+    Yb = bl.forward_batched(X, packed, gamma, K)
+    for l in (0, 1, L - 1):
+        Ys, acc = bl.forward(X[l], packed[l], gamma[l:l + 1], K, return_acc=True)
+        Y1 = bl.forward(X[l], packed[l], gamma[l:l + 1], K)
+        torch.cuda.synchronize()
+        assert torch.equal(Ys, Yb[l]) and torch.equal(Y1, Yb[l])
+        if l == 0:
+            ref = O.bitlinear_forward(P.X, P.W)
+            assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+            check_y(Ys.cpu().numpy(), ref["Y"])
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 2048, 2048), (8, 2048, 5632), (7, 1000, 300)])
+def test_split_form_equals_streaming_form_radix3(M, K, N):
+    L = 300
+    say(f"radix-3 decode split vs streaming M={M} K={K} N={N}")
+    P, X, packed, gamma = pool(L, M, K, N, seed=3 * M + K + N, fmt="radix3")
+    Yb, accb = bl.forward_r3(X, packed, gamma, K, return_acc=True)
+    for l in (0, L // 2):
+        Ys, acc = bl.forward_r3(X[l], packed[l], gamma[l:l + 1], K, return_acc=True)
+        torch.cuda.synchronize()
+        assert torch.equal(Ys, Yb[l]) and torch.equal(acc, accb[l])
+        if l == 0:
+            ref = O.bitlinear_forward(P.X, P.W)
+            assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+
+
+def test_split_form_relu2_epilogue():
+    """The FFN block's up projection (ReLU^2 epilogue) and its down projection
+    on copied codes take the split form for a single block."""
+    rng = np.random.default_rng(12)
+    X = rng.standard_normal((8, 512)).astype(np.float32)
+    Wu = (0.02 * rng.standard_normal((1408, 512))).astype(np.float32)
+    Wd = (0.02 * rng.standard_normal((512, 1408))).astype(np.float32)
+    up = bl.quantize_weights(torch.from_numpy(Wu).to(DEV))
+    down = bl.quantize_weights(torch.from_numpy(Wd).to(DEV))
+    Y, A = bl.ffn_forward(torch.from_numpy(X).to(DEV), up, down, path="decode", return_hidden=True)
+    Yp, Ap = bl.ffn_forward(torch.from_numpy(X).to(DEV), up, down, path="prefill", return_hidden=True)
+    torch.cuda.synchronize()
+    ref = O.ffn_forward(X, Wu, Wd)
+    assert np.array_equal(A.cpu().numpy(), ref["A"])
+    assert torch.equal(A, Ap) and torch.equal(Y, Yp)
+    check_y(Y.cpu().numpy(), ref["Y"])
