@@ -43,6 +43,12 @@ Every line also carries "attainable": what plain kernels reach on this GPU
 registers) beside the published peaks that "roofline" uses (--no-peaks skips
 them), and the CPU baseline names the host's CPU model.
 
+Without --warmup / --steps, each timed section warms up for at least 0.3 s
+under load (the GPU reaches its sustained state only after ~0.1-0.15 s of
+continuous work) and times at least 0.25 s (and at least 50 steps); the line
+reports the counts actually run.  Given on the command line, they are used
+exactly.
+
 Prints exactly one JSON line on stdout; progress goes to stderr.
 --copy-calibration runs a plain 1 GiB device copy (for HBM counter scaling).
 """
@@ -51,6 +57,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -139,6 +146,46 @@ class Timer:
         self.b.record()
         self.torch.cuda.synchronize()
         self.ms = self.a.elapsed_time(self.b)
+
+
+# Default warm-up and timed region, by time under load.  The GPU settles into
+# its sustained state only after about 0.1-0.15 s of continuous load (decode
+# streams ~3% faster after it; it falls back within a second of idling), so by
+# default the untimed warm-up runs for at least SETTLE_S and the timed region
+# for at least TIMED_S.  Explicit --warmup / --steps are used exactly as given.
+SETTLE_S = 0.3
+TIMED_S = 0.25
+MIN_STEPS = 50
+MIN_WARMUP = 5
+
+
+def plan_steps(args, torch, step):
+    """(warmup, steps) for this step function: the counts given on the command
+    line, else derived from the duration of one step (timed after one call)."""
+    if args.warmup is not None and args.steps is not None:
+        return args.warmup, args.steps
+    step()
+    with Timer(torch) as t:
+        step()
+    est = max(t.ms * 1e-3, 1e-6)
+    warmup = args.warmup if args.warmup is not None else min(100000, max(MIN_WARMUP, math.ceil(SETTLE_S / est)))
+    steps = args.steps if args.steps is not None else min(100000, max(MIN_STEPS, math.ceil(TIMED_S / est)))
+    return warmup, steps
+
+
+def run_timed(args, torch, step, what: str):
+    """Warm up, then time the step: (ms per step, warmup, steps)."""
+    warmup, steps = plan_steps(args, torch, step)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {what}: warmup done ({warmup} steps)")
+    with Timer(torch) as t:
+        for _ in range(steps):
+            step()
+    ms = t.ms / steps
+    log(f"[bench] {what}: timed {steps} steps, {ms * 1e3:.1f} us/step")
+    return ms, warmup, steps
 
 
 # ---------------------------------------------------------------------------
@@ -237,19 +284,11 @@ def bench_decode(args, torch, bl, dev):
         def single(l, out):
             bl.forward(X[l], packed[l], gamma[l:l + 1], K, out=out)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
-    with Timer(torch) as t:
-        for _ in range(args.steps):
-            step()
-    ms_step = t.ms / args.steps
+    ms_step, warmup, steps = run_timed(args, torch, step, "decode")
     step_bytes = L * (packed_bytes + M * K * 2 + M * N * 4)
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
     gw_s = L * N * K / (ms_step * 1e-3) / 1e9
-    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {gbps:.1f} GB/s, "
-        f"{gw_s:.1f} G weights/s")
+    log(f"[bench] decode: {gbps:.1f} GB/s, {gw_s:.1f} G weights/s")
 
     # one layer per call, rotating over the pool (cold weights): the latency-bound single call
     Y1 = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -265,7 +304,7 @@ def bench_decode(args, torch, bl, dev):
 
     out = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s",
-        "ms_per_step": round(ms_step, 6),
+        "ms_per_step": round(ms_step, 6), "warmup": warmup, "steps": steps,
         "dtype": "i8",
         "config": {"workload": f"{args.workload} x {L} layers per step (batched decode, cold weights)",
                    "M": M, "K": K, "N": N, "layers": L, "x_dtype": "bf16",
@@ -393,31 +432,28 @@ def bench_prefill(args, torch, bl, dev, workload=None):
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
     ws_bytes = bl.abi.load().bitlinear_forward_workspace_bytes(M, K)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
-    for _ in range(args.warmup):
+    def step():
         bl.forward(X, packed, gamma, K, out=Y, workspace=ws)
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
-    with Timer(torch) as t:
-        for _ in range(args.steps):
-            bl.forward(X, packed, gamma, K, out=Y, workspace=ws)
-    ms_step = t.ms / args.steps
+
+    ms_step, warmup, steps = run_timed(args, torch, step, f"prefill {workload}")
     ops = 2.0 * M * N * K
     tops = ops / (ms_step * 1e-3) / 1e12
-    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {tops:.1f} TOPS")
+    log(f"[bench] prefill {workload}: {tops:.1f} TOPS")
 
-    # dominant kernel alone: the GEMM + rescale from precomputed codes
+    # dominant kernel alone: the GEMM + rescale from precomputed codes, timed
+    # over as many calls right after the step's own timed region
     Xq, ga, rs = bl.quantize_activations(X)
     for _ in range(2):
         bl.forward_quantized(Xq, ga, rs, packed, gamma, K, out=Y)
     with Timer(torch) as tg:
-        for _ in range(args.steps):
+        for _ in range(steps):
             bl.forward_quantized(Xq, ga, rs, packed, gamma, K, out=Y)
-    gemm_ms = tg.ms / args.steps
+    gemm_ms = tg.ms / steps
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
     step_bytes = N * bl.packed_words(K) * 4 + M * K * 2 + M * N * 4
     out = {
         "metric": METRIC, "value": round(tops, 2), "unit": "TOPS",
-        "ms_per_step": round(ms_step, 6),
+        "ms_per_step": round(ms_step, 6), "warmup": warmup, "steps": steps,
         "dtype": "i8",
         "config": {"workload": workload, "M": M, "K": K, "N": N, "x_dtype": "bf16",
                    "ops_per_step": ops, "bytes_per_step": step_bytes},
@@ -448,7 +484,7 @@ def prefill_objects(args, torch, bl, dev) -> dict:
         cfg = o.pop("config")
         o.pop("metric")
         o = {"workload": w, "M": cfg["M"], "K": cfg["K"], "N": cfg["N"], "x_dtype": cfg["x_dtype"],
-             "ops_per_step": cfg["ops_per_step"], "steps": args.steps, **o}
+             "ops_per_step": cfg["ops_per_step"], **o}
         if "cpu_baseline" in o:
             o["cpu_baseline"].update(host_cpu())
         out[w] = o
@@ -527,32 +563,25 @@ def bench_ffn(args, torch, bl, dev):
     def step():
         bl.ffn_forward(X, (pu, gu), (pd, gd), out=Y, workspace=fws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
-    with Timer(torch) as t:
-        for _ in range(args.steps):
-            step()
-    ms_step = t.ms / args.steps
+    ms_step, warmup, steps = run_timed(args, torch, step, "FFN block")
     ops = 2.0 * 2 * M * D * F * L
     tops = ops / (ms_step * 1e-3) / 1e12
     # algorithmic bytes: packed weights, X, the hidden layer written and read, Y
     step_bytes = L * (wbytes + M * D * 2 + 2 * M * F * 4 + M * Do * 4)
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {gbps:.1f} GB/s, {tops:.1f} TOPS")
+    log(f"[bench] FFN block: {gbps:.1f} GB/s, {tops:.1f} TOPS")
     cfg = {"workload": args.workload + (f" x {L} layers per step (batched decode, cold weights)" if L > 1 else ""),
            "M": M, "D": D, "F": F, "D_out": Do, "layers": L, "x_dtype": "bf16", "path": "decode" if decode else "prefill",
            "bytes_per_step": step_bytes, "ops_per_step": ops}
     if decode:
         out = {"metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "ms_per_step": round(ms_step, 6),
-               "dtype": "i8", "config": cfg,
+               "warmup": warmup, "steps": steps, "dtype": "i8", "config": cfg,
                "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                             "kernel": "whole block: decode_kernel (up, ReLU^2 epilogue), activation quantiser over all hidden rows, decode_kernel (down, on those codes)"}}
     else:
         out = {"metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "ms_per_step": round(ms_step, 6),
-               "dtype": "i8", "config": cfg,
+               "warmup": warmup, "steps": steps, "dtype": "i8", "config": cfg,
                "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                             "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None,
                             "kernel": "whole block: 2 x (activation quantiser + prefill GEMM)"}}
@@ -618,18 +647,12 @@ def bench_backward(args, torch, bl, dev):
     def step():
         bl.backward(dY, packedT, gamma, Xq, ga, mask, K, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
-    with Timer(torch) as t:
-        for _ in range(args.steps):
-            step()
-    ms_step = t.ms / args.steps
+    ms_step, warmup, steps = run_timed(args, torch, step, "STE backward")
     flops = 2.0 * 2 * M * N * K
     tflops = flops / (ms_step * 1e-3) / 1e12
-    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
+    log(f"[bench] STE backward: {tflops:.1f} TFLOP/s")
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms_step, 6),
+           "warmup": warmup, "steps": steps,
            "dtype": "bf16",
            "config": {"workload": args.workload, "M": M, "K": K, "N": N, "flops_per_step": flops,
                       "note": "dX = gamma dY W_q and dW = (dY^T A_hat) * range mask, bf16 matrix cores"},
@@ -755,8 +778,11 @@ def copy_calibration(torch, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help=f"timed steps (default: enough for {TIMED_S} s, at least {MIN_STEPS})")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help=f"untimed warm-up steps (default: enough for {SETTLE_S} s under load, "
+                         f"at least {MIN_WARMUP})")
     ap.add_argument("--workload", default="decode_m1_k2048_n2048",
                     choices=sorted(DECODE_WORKLOADS) + list(PREFILL_WORKLOADS) + sorted(FFN_WORKLOADS)
                     + sorted(BACKWARD_WORKLOADS))
@@ -800,7 +826,7 @@ def main():
     else:
         out = bench_prefill(args, torch, bl, dev)
     line = {"metric": out.pop("metric"), "value": out.pop("value"), "unit": out.pop("unit"),
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "n_gpus": 1, "steps": out.pop("steps"), "warmup": out.pop("warmup"),
             "ms_per_step": out.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": out.pop("dtype"), "data": "synthetic (seeded)",
             "config": out.pop("config")}

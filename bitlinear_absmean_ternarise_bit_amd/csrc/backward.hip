@@ -173,8 +173,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
 // EPI 0: C * gamma;  EPI 1: C where bit q of row p of the range mask is set
 // (mask: rows of kw 32-bit words, bit q % 32 of word q / 32), else 0.
 //
-// Tile BM x BN, WM x WN waves each owning (BM/WM) x (BN/WN) = 64 x (BN/WN) of
-// 32 x 32 MFMA tiles; 64 r per LDS stage, two stages.  Global loads run two
+// Tile BM x BN, WM x WN waves each owning (BM/WM) x (BN/WN) (64 or 128 rows)
+// of 32 x 32 MFMA tiles; 64 r per LDS stage, two stages.  Global loads run two
 // stages ahead into two register sets, and the next stage is written to LDS
 // halfway through the contraction of the current one, so one barrier per
 // stage suffices and the matrix cores keep working while loads are in flight.
@@ -191,11 +191,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
   constexpr int THREADS = 64 * WM * WN;
   constexpr int A_BYTES = BM * ROWB;
   constexpr int STAGE = A_BYTES + BN * ROWB;
-  constexpr int MI = BM / WM / 32, NI = BN / WN / 32;
+  constexpr int WROWS = BM / WM;  // rows of a wave's tile
+  constexpr int MI = WROWS / 32, NI = BN / WN / 32;
   constexpr int A_LOADS = BM * 8 / THREADS;
-  constexpr int B_LOADS = BMODE == 0 ? BN * 8 / THREADS : 1;
-  static_assert(BM / WM == 64 && A_LOADS >= 1 && B_LOADS >= 1 && NI >= 1, "tile shape");
-  static_assert(BMODE == 0 || THREADS == 4 * BN, "packed B: one 32-bit word of a row's unit per thread");
+  constexpr int B_LOADS = BMODE == 0 ? BN * 8 / THREADS : BN * 4 / THREADS;  // 16-byte slots, or packed words
+  static_assert((WROWS == 64 || WROWS == 128) && A_LOADS >= 1 && B_LOADS >= 1 && NI >= 1, "tile shape");
+  static_assert(BMODE == 0 || (B_LOADS <= 4 && BN * 4 == B_LOADS * THREADS), "packed B: whole words per thread");
   __shared__ __align__(1024) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -244,13 +245,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
       b_dst[i] = A_BYTES + r * ROWB + 16 * (c ^ ((r >> 1) & 7));
     }
   }
-  // packed B: thread tid stages word tid % 4 of row tid / 4's unit (16 codes,
-  // two 16-byte slots of bf16), so the expansion is spread over every wave
+  // packed B: word s % 4 of row s / 4's unit (16 codes, two 16-byte slots of
+  // bf16) for s = tid + THREADS i, so the expansion is spread over every wave
   const uint32_t units = static_cast<uint32_t>(Rp >> 6);
-  const int pb_r = tid >> 2, pb_w = tid & 3;
-  const bool pb_row = BMODE == 1 && q0 + pb_r < Q;
+  const int pb_w = tid & 3;
 
-  v4u ra[2][A_LOADS], rb[2][B_LOADS];
+  v4u ra[2][A_LOADS], rb[2][BMODE == 0 ? B_LOADS : 1];  // packed B: word i in element i
   auto gload = [&](int it, auto set_tag) {
     constexpr int S = decltype(set_tag)::value;
 #pragma unroll
@@ -262,10 +262,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
         rb[S][i] =
             __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, b_off[i] == kOff ? kOff : b_off[i] + 128u * it, 0, 0);
     } else {
-      const uint32_t off = pb_row ? unit_offset(static_cast<uint32_t>(q0 + pb_r), static_cast<uint32_t>(it),
-                                                static_cast<uint32_t>(Q), units) + 4u * pb_w
-                                  : kOff;
-      rb[S][0][0] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_b, off, 0, 0);
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) {
+        const int r = (tid + THREADS * i) >> 2;
+        const uint32_t off = q0 + r < Q ? unit_offset(static_cast<uint32_t>(q0 + r), static_cast<uint32_t>(it),
+                                                      static_cast<uint32_t>(Q), units) + 4u * pb_w
+                                        : kOff;
+        rb[S][0][i] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_b, off, 0, 0);
+      }
     }
   };
   auto swrite = [&](char* st, auto set_tag) {
@@ -279,22 +283,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
       // 16 codes -> 16 bf16 values c - 1 through two byte tables (v_perm):
       // high bytes {0xBF, 0x00, 0x3F} and low bytes {0x80, 0x00, 0x80} for c = 0, 1, 2
       constexpr uint32_t kHi = 0x003F00BFu, kLo = 0x00800080u;
-      const int r = pb_r;
-      char* sb = st + A_BYTES + r * ROWB;
-      const uint32_t w = rb[S][0][0];
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {  // slot c = 2 pb_w + cc: k = 8c .. 8c + 7, fields i = 2 cc, 2 cc + 1
-        const int c = 2 * pb_w + cc;
-        v4u out;
+      for (int i = 0; i < B_LOADS; ++i) {
+        const int r = (tid + THREADS * i) >> 2;
+        char* sb = st + A_BYTES + r * ROWB;
+        const uint32_t w = rb[S][0][i];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t x = (w >> (2 * (2 * cc + h))) & 0x03030303u;
-          const uint32_t hi = __builtin_amdgcn_perm(0u, kHi, x);
-          const uint32_t lo = __builtin_amdgcn_perm(0u, kLo, x);
-          out[2 * h] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-          out[2 * h + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+        for (int cc = 0; cc < 2; ++cc) {  // slot c = 2 pb_w + cc: k = 8c .. 8c + 7, fields i = 2 cc, 2 cc + 1
+          const int c = 2 * pb_w + cc;
+          v4u out;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t x = (w >> (2 * (2 * cc + h))) & 0x03030303u;
+            const uint32_t hi = __builtin_amdgcn_perm(0u, kHi, x);
+            const uint32_t lo = __builtin_amdgcn_perm(0u, kLo, x);
+            out[2 * h] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+            out[2 * h + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+          }
+          *reinterpret_cast<v4u*>(sb + 16 * (c ^ ((r >> 1) & 7))) = out;
         }
-        *reinterpret_cast<v4u*>(sb + 16 * (c ^ ((r >> 1) & 7))) = out;
       }
     }
   };
@@ -314,7 +321,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int sw = 16 * ((2 * ks + lh) ^ ((lr >> 1) & 7));
-    a_rd[ks] = (wm * 64 + lr) * ROWB + sw;
+    a_rd[ks] = (wm * WROWS + lr) * ROWB + sw;
     b_rd[ks] = A_BYTES + (wn * (BN / WN) + lr) * ROWB + sw;
   }
   auto contract_half = [&](const char* st, int hs) {
@@ -368,7 +375,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
   // loop and keep them live (spilled) across it.  The outputs are written
   // nontemporally: they are not read again here, and streaming them evicts
   // less of the operand panels that other tiles on this XCD still read.
-  int lrow = wm * 64 + 4 * lh;
+  int lrow = wm * WROWS + 4 * lh;
   int lcol = wn * (BN / WN) + lr;
   asm volatile("" : "+v"(lrow), "+v"(lcol));
   const float g = gamma[0];

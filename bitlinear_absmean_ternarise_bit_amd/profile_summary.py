@@ -1,6 +1,7 @@
 """Markdown summaries of rocprofv3 output, for the profiles kept beside the code.
 
     python -m bitlinear_absmean_ternarise_bit_amd.profile_summary TRACE_DIR [--pmc DIR ...] [--match TEXT]
+        [--last N]
 
 TRACE_DIR holds the output of ``rocprofv3 --kernel-trace [--stats] -d TRACE_DIR``
 (the results database, or with ``--output-format csv`` the kernel-trace CSV);
@@ -8,7 +9,9 @@ each ``--pmc DIR`` the output of one ``rocprofv3 --pmc COUNTERS ... -d DIR
 --output-format csv`` run.  Prints, for every kernel (name shortened), the
 number of dispatches and the average / median / minimum / maximum duration,
 grouped by launch shape, and for the counter runs the per-dispatch average
-of every counter for the kernels whose name contains TEXT.
+of every counter for the kernels whose name contains TEXT.  --last N keeps,
+for every kernel and launch shape, only its last N dispatches in time order
+(the timed steps of a run whose warm-up came first).
 """
 from __future__ import annotations
 
@@ -26,24 +29,37 @@ def _short(name: str, width: int = 96) -> str:
     return name if len(name) <= width else name[: width - 3] + "..."
 
 
-def kernel_rows(trace_dir: str):
-    """(name, duration_us, grid_threads, workgroup, lds, vgpr, agpr) per dispatch."""
+def kernel_rows(trace_dir: str, last: int = 0):
+    """(name, duration_us, grid_threads, workgroup, lds, vgpr, agpr) per dispatch, in time
+    order; with last > 0 only the last `last` dispatches of every kernel and launch shape."""
     rows = []
     for db in glob.glob(os.path.join(trace_dir, "**", "*results.db"), recursive=True):
         con = sqlite3.connect(db)
-        for n, dur, gx, wx, lds, v, a in con.execute(
-                "select name, duration, grid_x, workgroup_x, lds_size, vgpr_count, accum_vgpr_count from kernels"):
-            rows.append((n, dur / 1000.0, gx, wx, lds, v, a))
+        for n, start, dur, gx, wx, lds, v, a in con.execute(
+                "select name, start, duration, grid_x, workgroup_x, lds_size, vgpr_count, accum_vgpr_count "
+                "from kernels"):
+            rows.append((start, n, dur / 1000.0, gx, wx, lds, v, a))
         con.close()
     for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
-                rows.append((r["Kernel_Name"], dur, int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0),
+                start = int(r["Start_Timestamp"])
+                dur = (int(r["End_Timestamp"]) - start) / 1000.0
+                rows.append((start, r["Kernel_Name"], dur, int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0),
                              int(r.get("Workgroup_Size", r.get("Workgroup_Size_X", 0)) or 0),
                              int(r.get("LDS_Block_Size", r.get("Lds_Size", 0)) or 0),
                              int(r.get("VGPR_Count", r.get("Arch_VGPR_Count", 0)) or 0),
                              int(r.get("Accum_VGPR_Count", 0) or 0)))
+    rows.sort(key=lambda r: r[0])
+    rows = [r[1:] for r in rows]
+    if last > 0:
+        groups = defaultdict(list)
+        for r in rows:
+            groups[(r[0],) + r[2:]].append(r)
+        keep = set()
+        for g in groups.values():
+            keep.update(id(r) for r in g[-last:])
+        rows = [r for r in rows if id(r) in keep]
     return rows
 
 
@@ -57,8 +73,8 @@ def counter_rows(pmc_dir: str):
     return out
 
 
-def summarise(trace_dir: str, pmc_dirs=(), match: str = "") -> str:
-    rows = kernel_rows(trace_dir)
+def summarise(trace_dir: str, pmc_dirs=(), match: str = "", last: int = 0) -> str:
+    rows = kernel_rows(trace_dir, last)
     lines = []
     by_name = defaultdict(list)
     by_shape = defaultdict(list)
@@ -99,8 +115,9 @@ def main():
     ap.add_argument("trace_dir")
     ap.add_argument("--pmc", action="append", default=[])
     ap.add_argument("--match", default="")
+    ap.add_argument("--last", type=int, default=0)
     args = ap.parse_args()
-    print(summarise(args.trace_dir, args.pmc, args.match))
+    print(summarise(args.trace_dir, args.pmc, args.match, args.last))
 
 
 if __name__ == "__main__":
