@@ -9,13 +9,18 @@
 // (the activation clip never binds; gamma and gamma_A are constants).
 // Training precision: dY and A_hat in bfloat16, float32 accumulation.
 //
-// Both contractions run on one bf16 MFMA GEMM, C[p, q] = sum_r A[p, r] B[q, r],
-// whose operands both have the contraction index contiguous:
-//   dX: A = dY (in place when its rows start on 16-byte boundaries, else a
-//       zero-padded copy), B = the ternary codes of W^T, packed in
-//       the 2-bit format (pack_transposed_kernel) and expanded to bf16 {-1,0,1}
-//       while they are staged into LDS;
-//   dW: A = dY^T, B = A_hat^T (transposed copies, zero-padded along M).
+// dX runs on a bf16 MFMA GEMM, C[p, q] = sum_r A[p, r] B[q, r], whose operands
+// both have the contraction index contiguous: A = dY (in place when its rows
+// start on 16-byte boundaries, else a zero-padded copy), B = the ternary codes
+// of W^T, packed in the 2-bit format (pack_transposed_kernel) and expanded to
+// bf16 {-1,0,1} while they are staged into LDS.
+// dW contracts over the tokens, the row index of both dY and A_hat.  When dY
+// has N % 8 == 0 and 16-byte aligned rows (and so do the codes), it is read
+// as it lies, A_hat is formed once in that layout, and the matrix-core
+// operands come from gfx950's transposing LDS reads (bf16_gemm_tn_kernel);
+// otherwise dY^T and A_hat^T are copied out (zero-padded along M) for the
+// first GEMM.  Both give the same bits: the matrix cores see the same operands
+// in the same order.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -26,6 +31,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 64;  // transpose / pack tiles
 
@@ -162,6 +169,46 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
     out.x = w[0]; out.y = w[1]; out.z = w[2]; out.w = w[3];
     if (m0 + 8 * c < Mp) *reinterpret_cast<uint4*>(dst + r * Mp + m0 + 8 * c) = out;
   }
+}
+
+// Masked store of a finished tile: C[p, q] = acc where bit q of row p of the
+// range mask is set, else 0.  The lane holds rows lrow + 32 i + 8 (e / 4) +
+// e % 4 and columns lcol + 32 j of the tile.  The tile's mask words go into
+// LDS first (every wave is past the last stage's LDS reads): vector-memory
+// operations complete in order, so mask loads interleaved with the output
+// stores would each wait for the stores before them.  The outputs are written
+// nontemporally: they are not read again here, and streaming them evicts less
+// of the operand panels that other tiles on this XCD still read.
+template <int BM, int BN, int THREADS, int MI, int NI>
+__device__ __forceinline__ void store_masked(const f32x16 (&acc)[MI][NI], char* smem, int tid, int lrow, int lcol,
+                                             int lr, int64_t p0, int64_t q0, int64_t P, int64_t Q,
+                                             float* __restrict__ C, int64_t ldc, const uint32_t* __restrict__ mask,
+                                             int64_t kw) {
+  constexpr int WPR32 = BN / 32;  // mask words per tile row
+  uint32_t* mb = reinterpret_cast<uint32_t*>(smem);
+  const int64_t w0 = q0 >> 5;
+  for (int idx = tid; idx < BM * WPR32; idx += THREADS) {
+    const int row = idx / WPR32, wi = idx % WPR32;
+    const int64_t p = p0 + row, w = w0 + wi;
+    mb[idx] = (p < P && w < kw) ? mask[p * kw + w] : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = lrow + i * 32 + 8 * (e >> 2) + (e & 3);
+      const int64_t p = p0 + row;
+      if (p >= P) continue;
+      // bit lr of words (row, lcol / 32 + j): columns lcol + 32 j
+      const uint32_t* wrow = mb + row * WPR32 + (lcol >> 5);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int64_t q = q0 + lcol + j * 32;
+        if (q >= Q) continue;
+        __builtin_nontemporal_store((wrow[j] >> lr) & 1u ? acc[i][j][e] : 0.0f, C + p * ldc + q);
+      }
+    }
 }
 
 // bf16 MFMA GEMM, C[p, q] = sum_r A[p, r] B[q, r] over r < Rp (a multiple of 64).
@@ -373,13 +420,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
   // 32 x 32 tile.  The lane's first row and column are opaque to the
   // compiler, so it does not compute the output addresses before the main
   // loop and keep them live (spilled) across it.  The outputs are written
-  // nontemporally: they are not read again here, and streaming them evicts
-  // less of the operand panels that other tiles on this XCD still read.
+  // nontemporally (see store_masked).
   int lrow = wm * WROWS + 4 * lh;
   int lcol = wn * (BN / WN) + lr;
   asm volatile("" : "+v"(lrow), "+v"(lcol));
-  const float g = gamma[0];
   if constexpr (EPI == 0) {
+    const float g = gamma[0];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -393,35 +439,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_nt_kernel(
         }
       }
   } else {
-    // The tile's mask words go into LDS first (every wave is past the last
-    // stage's LDS reads): vector-memory operations complete in order, so
-    // mask loads interleaved with the output stores would each wait for the
-    // stores before them.
-    constexpr int WPR32 = BN / 32;  // mask words per tile row
-    uint32_t* mb = reinterpret_cast<uint32_t*>(smem);
-    const int64_t w0 = q0 >> 5;
-    for (int idx = tid; idx < BM * WPR32; idx += THREADS) {
-      const int row = idx / WPR32, wi = idx % WPR32;
-      const int64_t p = p0 + row, w = w0 + wi;
-      mb[idx] = (p < P && w < kw) ? mask[p * kw + w] : 0u;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = lrow + i * 32 + 8 * (e >> 2) + (e & 3);
-        const int64_t p = p0 + row;
-        if (p >= P) continue;
-        // bit lr of words (row, lcol / 32 + j): columns lcol + 32 j
-        const uint32_t* wrow = mb + row * WPR32 + (lcol >> 5);
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          const int64_t q = q0 + lcol + j * 32;
-          if (q >= Q) continue;
-          __builtin_nontemporal_store((wrow[j] >> lr) & 1u ? acc[i][j][e] : 0.0f, C + p * ldc + q);
-        }
-      }
+    store_masked<BM, BN, THREADS, MI, NI>(acc, smem, tid, lrow, lcol, lr, p0, q0, P, Q, C, ldc, mask, kw);
   }
 }
 
@@ -433,6 +451,219 @@ void launch_gemm(const uint16_t* A, int64_t P, int64_t lda, const void* B, int64
   bf16_gemm_nt_kernel<BM, BN, WM, WN, BMODE, EPI><<<static_cast<unsigned>(tiles_p * tiles_q), 64 * WM * WN, 0,
                                                     stream>>>(A, P, lda, B, Q, Rp, C, ldc, gamma, mask, kw, bytes_a,
                                                               bytes_b, tiles_p, tiles_q);
+}
+
+
+// A_hat = bf16(fp32(fp32(gamma_a[m] / 127) * Xq[m, k])) (round half to even),
+// r-major [M, ld] with ld a multiple of 8; 16 codes per thread and step.
+// Columns K .. ld - 1 hold whatever the codes' padding gives: they meet only
+// outputs past K.
+__global__ __launch_bounds__(256) void ahat_kernel(const int8_t* __restrict__ Xq, int64_t M, int64_t ldq,
+                                                   int64_t ld, const float* __restrict__ gamma_a,
+                                                   uint16_t* __restrict__ out) {
+  const int64_t cpr = ld / 16 + (ld % 16 ? 1 : 0);  // 16-code chunks per row (the last may be half)
+  const int64_t total = M * cpr;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t m = i / cpr, c = i - m * cpr;
+    const uint4 w = *reinterpret_cast<const uint4*>(Xq + m * ldq + 16 * c);
+    const float sc = __fdiv_rn(gamma_a[m], 127.0f);
+    const float bias = -128.0f * sc;
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    uint32_t h[8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint32_t u = wd[x] ^ 0x80808080u;
+      const f32x2 lo = {__fmaf_rn(sc, static_cast<float>(u & 0xffu), bias),
+                        __fmaf_rn(sc, static_cast<float>((u >> 8) & 0xffu), bias)};
+      const f32x2 hi = {__fmaf_rn(sc, static_cast<float>((u >> 16) & 0xffu), bias),
+                        __fmaf_rn(sc, static_cast<float>(u >> 24), bias)};
+      h[2 * x] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+      h[2 * x + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+    }
+    uint16_t* dst = out + m * ld + 16 * c;
+    *reinterpret_cast<uint4*>(dst) = uint4{h[0], h[1], h[2], h[3]};
+    if (16 * c + 8 < ld) *reinterpret_cast<uint4*>(dst + 8) = uint4{h[4], h[5], h[6], h[7]};
+  }
+}
+
+// dW without transposed copies: C[p, q] = sum_r A[r, p] B[r, q] * mask, with
+// both operands r-major: A = dY as it lies (bf16 [R, P]) and B = A_hat from
+// ahat_kernel (bf16 [R, ldb]), rows 16-byte aligned.  Forming A_hat once
+// costs less than forming it in every tile (the 43 row tiles of a 11008-row
+// dW would each repeat it).  An LDS stage holds 64 r-rows of both tiles in
+// that layout; the matrix cores' operand (8
+// consecutive r of one column per lane) comes from two transposing LDS reads
+// (ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte rows that lanes 4 j + i / 4 address, j = 0..3).  For
+// 32 x 32 x 16 operands, lane l = 16 g + i addresses r-row 8 (g / 2) + 4 s +
+// i / 4 of the k step (read s = 0, 1) and columns 16 (g % 2) + 4 (i % 4) of
+// its 32-column block.  One such read touches 8 r-rows x 64 bytes; 16-byte
+// chunk c of row r is stored at chunk c ^ 4 (r % 4), so rows r .. r + 3 fall
+// on distinct quarters of the LDS banks.  Tiles, waves, the two-stage
+// pipeline and the epilogue are those of bf16_gemm_nt_kernel.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void bf16_gemm_tn_kernel(
+    const uint16_t* __restrict__ A, int64_t R, int64_t P, const uint16_t* __restrict__ B, int64_t ldb, int64_t Q,
+    float* __restrict__ C, int64_t ldc, const uint32_t* __restrict__ mask, int64_t kw, int bytes_a, int bytes_b,
+    int tiles_p, int tiles_q) {
+  constexpr int BK = 64;
+  constexpr int THREADS = 64 * WM * WN;
+  constexpr int ROWA = BM * 2, ROWB = BN * 2;  // LDS bytes of one r-row of each tile
+  constexpr int A_BYTES = BK * ROWA;
+  constexpr int STAGE = A_BYTES + BK * ROWB;
+  constexpr int WROWS = BM / WM;
+  constexpr int MI = WROWS / 32, NI = BN / WN / 32;
+  constexpr int A_CPR = BM / 8, B_CPR = BN / 8;  // 16-byte chunks per row
+  constexpr int A_LOADS = BK * A_CPR / THREADS;
+  constexpr int B_LOADS = BK * B_CPR / THREADS;
+  static_assert((WROWS == 64 || WROWS == 128) && NI >= 1 && A_LOADS >= 1 && B_LOADS >= 1 &&
+                    BK * A_CPR == A_LOADS * THREADS && BK * B_CPR == B_LOADS * THREADS,
+                "tile shape");
+  __shared__ __align__(1024) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int num_tiles = tiles_p * tiles_q;
+  int t = blockIdx.x;
+  if (num_tiles % 8 == 0) t = (t & 7) * (num_tiles >> 3) + (t >> 3);
+  constexpr int GROUP = 8;
+  const int group = t / (GROUP * tiles_q);
+  const int first_p = group * GROUP;
+  const int gsize = min(tiles_p - first_p, GROUP);
+  const int in_group = t - group * GROUP * tiles_q;
+  const int64_t p0 = static_cast<int64_t>(first_p + in_group % gsize) * BM;
+  const int64_t q0 = static_cast<int64_t>(in_group / gsize) * BN;
+
+  const int niter = static_cast<int>((R + BK - 1) / BK);
+  const uint32_t rowbytes_a = static_cast<uint32_t>(P) * 2u;
+  const uint32_t rowbytes_b = static_cast<uint32_t>(ldb) * 2u;
+
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0, bytes_a, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_b =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(B), 0, bytes_b, 0x00020000);
+  constexpr uint32_t kOff = 0x80000000u;  // past every resource: reads zeros
+
+  // chunk s = tid + THREADS i of a stage: A row s / A_CPR, column chunk
+  // s % A_CPR; B likewise.  The
+  // rows of thread tid step by THREADS / CPR per i, the chunk stays, and so
+  // does row % 4 (THREADS / CPR is a multiple of 4): one global offset and one
+  // LDS offset per operand, plus multiples of the row pitch.  Rows past R read
+  // zeros through the resources' range (R * row bytes); it goes in voffset,
+  // which the range check covers.
+  static_assert((THREADS / A_CPR) % 4 == 0 && (THREADS / B_CPR) % 4 == 0, "row step keeps row % 4");
+  constexpr int A_RSTEP = THREADS / A_CPR, B_RSTEP = THREADS / B_CPR;
+  const int ar = tid / A_CPR, ac = tid % A_CPR, br = tid / B_CPR, bc = tid % B_CPR;
+  const bool a_ok = p0 + 8 * ac < P, b_ok = q0 + 8 * bc < ldb;
+  const uint32_t a_off = static_cast<uint32_t>(ar) * rowbytes_a + static_cast<uint32_t>(p0 + 8 * ac) * 2u;
+  const uint32_t b_off = static_cast<uint32_t>(br) * rowbytes_b + static_cast<uint32_t>(q0 + 8 * bc) * 2u;
+  const int a_dst = ar * ROWA + 16 * (ac ^ (4 * (ar & 3)));
+  const int b_dst = A_BYTES + br * ROWB + 16 * (bc ^ (4 * (br & 3)));
+
+  v4u ra[2][A_LOADS], rb[2][B_LOADS];
+  auto gload = [&](int it, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
+    const uint32_t ra0 = static_cast<uint32_t>(it) * BK * rowbytes_a;
+    const uint32_t rb0 = static_cast<uint32_t>(it) * BK * rowbytes_b;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+      ra[S][i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc_a, a_ok ? a_off + ra0 + static_cast<uint32_t>(i * A_RSTEP) * rowbytes_a : kOff, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i)
+      rb[S][i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc_b, b_ok ? b_off + rb0 + static_cast<uint32_t>(i * B_RSTEP) * rowbytes_b : kOff, 0, 0);
+  };
+  auto swrite = [&](char* st, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<v4u*>(st + a_dst + i * A_RSTEP * ROWA) = ra[S][i];
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<v4u*>(st + b_dst + i * B_RSTEP * ROWB) = rb[S][i];
+  };
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // this lane's transposing-read offsets (k step 0, read 0) for each block;
+  // k step ks and read s add (16 ks + 4 s) rows, which keeps r % 4
+  const int g = lane >> 4, li = lane & 15;
+  const int rrow = 8 * (g >> 1) + (li >> 2);
+  const int cin = 2 * (g & 1) + ((li & 3) >> 1);  // chunk within the 32-column block
+  const int swz = 4 * (li >> 2);
+  int a_rd[MI], b_rd[NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+    a_rd[i] = rrow * ROWA + 16 * ((((wm * WROWS + 32 * i) >> 3) ^ swz) + cin) + 8 * (li & 1);
+#pragma unroll
+  for (int j = 0; j < NI; ++j)
+    b_rd[j] = A_BYTES + rrow * ROWB + 16 * ((((wn * (BN / WN) + 32 * j) >> 3) ^ swz) + cin) + 8 * (li & 1);
+
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  auto tr_operand = [&](const char* base) -> bf16x8 {
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + 4 * ROWA));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto tr_operand_b = [&](const char* base) -> bf16x8 {
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + 4 * ROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto contract_half = [&](const char* st, int hs) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ks = 2 * hs + kk;
+      bf16x8 a[MI], b[NI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) a[i] = tr_operand(st + a_rd[i] + 16 * ks * ROWA);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) b[j] = tr_operand_b(st + b_rd[j] + 16 * ks * ROWB);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  gload(0, S0());
+  gload(min(1, niter - 1), S1());
+  swrite(smem, S0());
+  gload(min(2, niter - 1), S0());
+  __syncthreads();
+  auto iteration = [&](int it, auto set_tag) {
+    const char* cur = smem + (it & 1) * STAGE;
+    char* nxt = smem + ((it + 1) & 1) * STAGE;
+    contract_half(cur, 0);
+    swrite(nxt, set_tag);
+    gload(min(it + 3, niter - 1), set_tag);
+    contract_half(cur, 1);
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it + 1 < niter; it += 2) {
+    iteration(it, S1());
+    iteration(it + 1, S0());
+  }
+  if (it < niter) iteration(it, S1());
+
+  const int lr = lane & 31, lh = lane >> 5;
+  int lrow = wm * WROWS + 4 * lh;
+  int lcol = wn * (BN / WN) + lr;
+  asm volatile("" : "+v"(lrow), "+v"(lcol));
+  store_masked<BM, BN, THREADS, MI, NI>(acc, smem, tid, lrow, lcol, lr, p0, q0, P, Q, C, ldc, mask, kw);
 }
 
 }  // namespace
@@ -467,7 +698,21 @@ hipError_t launch_backward(const uint16_t* dY, int64_t M, int64_t N, int64_t K, 
                                       nullptr, 0, static_cast<int>(M * (direct ? N : Np) * 2),
                                       static_cast<int>(K * (Np / 4)), stream);
   }
-  if (dW) {
+  if (dW && N % 8 == 0 && reinterpret_cast<uintptr_t>(dY) % 16 == 0 && reinterpret_cast<uintptr_t>(Xq) % 16 == 0) {
+    // operands as they are: no transposed copies
+    constexpr int BM = 256, BN = 256;
+    const int tiles_p = static_cast<int>((N + BM - 1) / BM), tiles_q = static_cast<int>((K + BN - 1) / BN);
+    const unsigned grid = static_cast<unsigned>(tiles_p * tiles_q);
+    // A_hat once, r-major with rows of K rounded up to 8, in the space of the
+    // transposed copies (dYt and At, contiguous: N Mp + K Mp >= M (K + 7) for N >= 8)
+    const int64_t ld = (K + 7) / 8 * 8;
+    int64_t blocks = (M * ((ld + 15) / 16) + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    ahat_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(Xq, M, Kp, ld, gamma_a, dYt);
+    bf16_gemm_tn_kernel<BM, BN, 4, 2><<<grid, 512, 0, stream>>>(dY, M, N, dYt, ld, K, dW, K, mask, mask_words(K),
+                                                               static_cast<int>(M * N * 2),
+                                                               static_cast<int>(M * ld * 2), tiles_p, tiles_q);
+  } else if (dW) {
     const dim3 g0(static_cast<unsigned>((N + kTile - 1) / kTile), static_cast<unsigned>(Mp / kTile));
     transpose_kernel<0><<<g0, 256, 0, stream>>>(dY, M, N, N, nullptr, dYt, Mp);
     const dim3 g1(static_cast<unsigned>((K + kTile - 1) / kTile), static_cast<unsigned>(Mp / kTile));

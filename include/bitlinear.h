@@ -274,7 +274,8 @@ int bitlinear_pack_transposed(const float* W, int64_t N, int64_t K, const float*
                               uint32_t* packedT, uint32_t* mask, void* stream);
 
 /* Workspace bytes of bitlinear_backward: padded and transposed bf16 copies of
- * dY and A_hat (about 2 M (2N + K) bytes). */
+ * dY and A_hat (about 2 M (2N + K) bytes; when N % 8 == 0 and dY and Xq are
+ * 16-byte aligned only A_hat is formed there, untransposed). */
 size_t bitlinear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*

@@ -76,7 +76,8 @@ def test_pack_transposed_bit_exact(N, K):
     assert torch.equal(pT, pT_only)
 
 
-BWD_CASES = [(1, 64, 64), (37, 300, 130), (128, 256, 192), (200, 1000, 520), (65, 130, 1100), (300, 64, 7)]
+BWD_CASES = [(1, 64, 64), (37, 300, 130), (128, 256, 192), (200, 1000, 520), (65, 130, 1100), (300, 64, 7),
+             (77, 2000, 264), (513, 96, 1032)]
 
 
 @pytest.mark.parametrize("M,K,N", BWD_CASES)
@@ -97,6 +98,24 @@ def test_backward_parity(M, K, N):
     bound_check(got_w, ref["dW"], absW, M)
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 64, 64), (77, 2000, 264), (513, 96, 1032), (200, 1000, 520), (64, 512, 8)])
+def test_backward_dw_paths_agree(M, K, N):
+    """dW from dY and the codes as they lie (rows 16-byte aligned, N % 8 == 0)
+    and from transposed copies (dY at an address that is not 16-byte
+    aligned) are the same bits: both feed the matrix cores the same operands
+    in the same order.  dX likewise (dY read in place vs a padded copy)."""
+    say(f"backward dW paths M={M} K={K} N={N}")
+    P, W, dY, gamma, Xq, ga, packedT, mask, dYd = setup(M, K, N, seed=3 * M + K + N)
+    flat = torch.empty((M * N + 8,), dtype=torch.bfloat16, device=DEV)
+    dYu = flat[1:1 + M * N].view(M, N)  # 2 bytes past a 16-byte boundary
+    dYu.copy_(dYd)
+    assert dYu.data_ptr() % 16 != 0 and dYd.data_ptr() % 16 == 0
+    dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, mask, K)
+    dXu, dWu = bl.backward(dYu, packedT, gamma, Xq, ga, mask, K)
+    torch.cuda.synchronize()
+    assert torch.equal(dW, dWu) and torch.equal(dX, dXu)
+
+
 def test_backward_one_output_at_a_time():
     P, W, dY, gamma, Xq, ga, packedT, mask, dYd = setup(50, 200, 90, seed=7)
     dX, dW = bl.backward(dYd, packedT, gamma, Xq, ga, mask, 200)
@@ -105,6 +124,28 @@ def test_backward_one_output_at_a_time():
     torch.cuda.synchronize()
     assert n1 is None and n2 is None
     assert torch.equal(dX, dX1) and torch.equal(dW, dW2)
+
+
+def test_backward_in_graph():
+    """Captured into a HIP graph, replays match the eager call, with eager
+    work and synchronisations between the replays."""
+    P, W, dY, gamma, Xq, ga, packedT, mask, dYd = setup(256, 512, 640, seed=10)
+    ws = torch.empty((abi.load().bitlinear_backward_workspace_bytes(256, 640, 512),), dtype=torch.uint8,
+                     device=DEV)
+    dX0, dW0 = bl.backward(dYd, packedT, gamma, Xq, ga, mask, 512, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dXg, dWg = bl.backward(dYd, packedT, gamma, Xq, ga, mask, 512, workspace=ws)
+    for i in range(3):
+        dXg.zero_()
+        dWg.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dXg, dX0) and torch.equal(dWg, dW0), i
+        e1, e2 = bl.backward(dYd, packedT, gamma, Xq, ga, mask, 512, workspace=ws)  # eager work between
+        torch.cuda.synchronize()
+        assert torch.equal(e1, dX0) and torch.equal(e2, dW0)
 
 
 def test_backward_7b_ffn_shape_full():
