@@ -508,8 +508,9 @@ def cpu_baseline_prefill(P, seconds):
     ops = 2.0 * reps * rows_per_rep * P.N * P.K
     log(f"[bench] cpu oracle: {reps} x {rows_per_rep} tokens in {el:.1f} s")
     return {"value": round(ops / el / 1e12, 6), "unit": "TOPS", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"{reps * rows_per_rep} of {P.M} tokens x all {P.N} outputs of {P.name}: "
-                      f"the oracle's forward from ternary codes, {rows_per_rep} tokens per call"}
+            "sample": f"{reps} calls of {rows_per_rep} tokens x all {P.N} outputs of {P.name} "
+                      f"({reps * rows_per_rep} token rows, cycling over its {P.M} tokens): "
+                      f"the oracle's forward from ternary codes"}
 
 
 # ---------------------------------------------------------------------------

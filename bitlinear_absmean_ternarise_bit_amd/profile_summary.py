@@ -1,7 +1,7 @@
 """Markdown summaries of rocprofv3 output, for the profiles kept beside the code.
 
     python -m bitlinear_absmean_ternarise_bit_amd.profile_summary TRACE_DIR [--pmc DIR ...] [--match TEXT]
-        [--last N]
+        [--last N [--ref TEXT]]
 
 TRACE_DIR holds the output of ``rocprofv3 --kernel-trace [--stats] -d TRACE_DIR``
 (the results database, or with ``--output-format csv`` the kernel-trace CSV);
@@ -9,9 +9,15 @@ each ``--pmc DIR`` the output of one ``rocprofv3 --pmc COUNTERS ... -d DIR
 --output-format csv`` run.  Prints, for every kernel (name shortened), the
 number of dispatches and the average / median / minimum / maximum duration,
 grouped by launch shape, and for the counter runs the per-dispatch average
-of every counter for the kernels whose name contains TEXT.  --last N keeps,
-for every kernel and launch shape, only its last N dispatches in time order
-(the timed steps of a run whose warm-up came first).
+of every counter for the kernels whose name contains TEXT.
+
+--last N keeps only the timed region of a run whose warm-up came first: the
+span of the last N dispatches of the reference launch (the launch shape,
+among kernels whose name contains --ref TEXT, with the most total time; by
+default the kernel with the most total time), extended over the dispatches
+that follow it directly while their names still contain TEXT (a step made of
+several launches of one kernel family).  Every dispatch that starts inside
+that span is kept, whatever its kernel.
 """
 from __future__ import annotations
 
@@ -29,9 +35,9 @@ def _short(name: str, width: int = 96) -> str:
     return name if len(name) <= width else name[: width - 3] + "..."
 
 
-def kernel_rows(trace_dir: str, last: int = 0):
+def kernel_rows(trace_dir: str, last: int = 0, ref: str = ""):
     """(name, duration_us, grid_threads, workgroup, lds, vgpr, agpr) per dispatch, in time
-    order; with last > 0 only the last `last` dispatches of every kernel and launch shape."""
+    order; with last > 0 only those inside the timed region (see the module notes)."""
     rows = []
     for db in glob.glob(os.path.join(trace_dir, "**", "*results.db"), recursive=True):
         con = sqlite3.connect(db)
@@ -51,16 +57,27 @@ def kernel_rows(trace_dir: str, last: int = 0):
                              int(r.get("VGPR_Count", r.get("Arch_VGPR_Count", 0)) or 0),
                              int(r.get("Accum_VGPR_Count", 0) or 0)))
     rows.sort(key=lambda r: r[0])
-    rows = [r[1:] for r in rows]
-    if last > 0:
-        groups = defaultdict(list)
+    if last > 0 and rows:
+        total = defaultdict(float)
         for r in rows:
-            groups[(r[0],) + r[2:]].append(r)
-        keep = set()
-        for g in groups.values():
-            keep.update(id(r) for r in g[-last:])
-        rows = [r for r in rows if id(r) in keep]
-    return rows
+            if not ref or ref in r[1]:
+                total[(r[1],) + r[3:]] += r[2]
+        if not ref:  # the kernel (any shape) with the most time, then its largest shape
+            by_name = defaultdict(float)
+            for k, v in total.items():
+                by_name[k[0]] += v
+            top = max(by_name, key=by_name.get)
+            total = {k: v for k, v in total.items() if k[0] == top}
+            ref = top
+        shape = max(total, key=total.get)
+        idx = [i for i, r in enumerate(rows) if (r[1],) + r[3:] == shape]
+        first, end = idx[-min(last, len(idx))], idx[-1]
+        while end + 1 < len(rows) and ref in rows[end + 1][1]:
+            end += 1
+        t0 = rows[first][0]
+        t1 = rows[end][0]
+        rows = [r for r in rows if t0 <= r[0] <= t1]
+    return [r[1:] for r in rows]
 
 
 def counter_rows(pmc_dir: str):
@@ -73,8 +90,8 @@ def counter_rows(pmc_dir: str):
     return out
 
 
-def summarise(trace_dir: str, pmc_dirs=(), match: str = "", last: int = 0) -> str:
-    rows = kernel_rows(trace_dir, last)
+def summarise(trace_dir: str, pmc_dirs=(), match: str = "", last: int = 0, ref: str = "") -> str:
+    rows = kernel_rows(trace_dir, last, ref)
     lines = []
     by_name = defaultdict(list)
     by_shape = defaultdict(list)
@@ -116,8 +133,9 @@ def main():
     ap.add_argument("--pmc", action="append", default=[])
     ap.add_argument("--match", default="")
     ap.add_argument("--last", type=int, default=0)
+    ap.add_argument("--ref", default="")
     args = ap.parse_args()
-    print(summarise(args.trace_dir, args.pmc, args.match, args.last))
+    print(summarise(args.trace_dir, args.pmc, args.match, args.last, args.ref))
 
 
 if __name__ == "__main__":
