@@ -201,6 +201,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const uint32_t R = N32 > n0 ? min(16u, N32 - n0) : 0u;  // rows of the block
     const uint32_t blk = n0 * units32 * 16u;
     const bool row_ok = valid && static_cast<uint32_t>(j) < R;
+    if constexpr (FMT == 3) {
+      // Radix-3 is bound by the vector ALU, so its offsets are formed with
+      // fewer operations: chunks before the last hold 4 units, so chunk cs of
+      // lane (j, g) is at blk + 64 R cs + 16 (4 j + g), linear in cs; the last
+      // chunk holds W = units - 4 last units (lanes j W + g, none for g >= W).
+      // (For the memory-bound 2-bit decode the general form below streams
+      // faster, so it keeps it.)
+      const uint32_t cs0 = static_cast<uint32_t>(c_lo + cb * kUnroll);
+      const uint32_t base = blk + cs0 * R * 64u + (4u * j + g) * 16u;
+      const uint32_t last = (units32 - 1u) >> 2;
+      const uint32_t Wl = units32 - 4u * last;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t cs = cs0 + static_cast<uint32_t>(u);
+        uint32_t off = base + static_cast<uint32_t>(u) * R * 64u;
+        if (cs == last) off = off - (4u * j + g) * 16u + (j * Wl + g) * 16u;
+        const bool ok = row_ok && cs <= last && (cs < last || g < Wl) &&
+                        (!SPLIT || cs < static_cast<uint32_t>(c_hi));
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, ok ? off : kOff, 0, kNontemporal);
+        r[u] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint32_t cs = static_cast<uint32_t>(c_lo + cb * kUnroll + u);
