@@ -492,8 +492,8 @@ __global__ __launch_bounds__(256) void ahat_kernel(const int8_t* __restrict__ Xq
 // ahat_kernel (bf16 [R, ldb]), rows 16-byte aligned.  Forming A_hat once
 // costs less than forming it in every tile (the 43 row tiles of a 11008-row
 // dW would each repeat it).  An LDS stage holds 64 r-rows of both tiles in
-// that layout; the matrix cores' operand (8
-// consecutive r of one column per lane) comes from two transposing LDS reads
+// that layout; the matrix cores' operand (8 consecutive r of one column per
+// lane) comes from two transposing LDS reads
 // (ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
 // i % 4 of the 8-byte rows that lanes 4 j + i / 4 address, j = 0..3).  For
 // 32 x 32 x 16 operands, lane l = 16 g + i addresses r-row 8 (g / 2) + 4 s +
