@@ -727,12 +727,18 @@ def attainable_peaks(torch, bl, dev, read_blocks: int = 2048, mfma_iters: int = 
     ms_mfma = timed(lambda: call("bitlinear_probe_mfma_i8", lib.bitlinear_probe_mfma_i8(
         mfma_iters, 2 * cus, mout.data_ptr(), stream)), reps=3)
     ops = 2 * cus * 4 * 8 * mfma_iters * 65536
-    del buf, out, mout
+    fout = torch.empty(2 * cus * 256, dtype=torch.float32, device=dev)
+    ms_bf16 = timed(lambda: call("bitlinear_probe_mfma_bf16", lib.bitlinear_probe_mfma_bf16(
+        mfma_iters, 2 * cus, fout.data_ptr(), stream)), reps=3)
+    flops = 2 * cus * 4 * 8 * mfma_iters * 32768
+    del buf, out, mout, fout
     return {"hbm_read_GBps": round(nbytes / ms_read / 1e6, 1),
             "hbm_copy_GBps": round(nbytes / ms_copy / 1e6, 1),
             "mfma_i8_TOPS": round(ops / ms_mfma / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(flops / ms_bf16 / 1e9, 1),
             "note": "plain kernels on this GPU: 1 GiB streaming read; 512 MiB copy (GB/s of bytes read "
-                    "+ written); independent v_mfma_i32_32x32x32_i8 on registers"}
+                    "+ written); independent v_mfma_i32_32x32x32_i8, and v_mfma_f32_32x32x16_bf16, on "
+                    "registers"}
 
 
 def cpu_model() -> str:

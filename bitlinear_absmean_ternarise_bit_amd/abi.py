@@ -69,6 +69,7 @@ NOALLOC_SCRATCH_BYTES = 80 * 1024 * 1024  # BITLINEAR_NOALLOC_SCRATCH_BYTES
 PROBE_SIGNATURES = {
     "bitlinear_probe_stream": (_int, [_p, _p, _i64, _int, _p, _p]),
     "bitlinear_probe_mfma_i8": (_int, [_int, _int, _p, _p]),
+    "bitlinear_probe_mfma_bf16": (_int, [_int, _int, _p, _p]),
 }
 
 _LIB = None

@@ -87,6 +87,37 @@ __global__ __launch_bounds__(256, 2) void mfma_i8_kernel(int iters, int32_t* __r
   out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = s;
 }
 
+// The same with v_mfma_f32_32x32x16_bf16 (32768 flops each) on eight
+// independent float accumulators.  The operands are small integers, so every
+// product and partial sum is exact and the result does not depend on the
+// accumulation order.
+typedef __bf16 probe_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float probe_f32x16 __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(256, 2) void mfma_bf16_kernel(int iters, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  probe_bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(static_cast<float>((lane + i) & 3));
+    b[i] = static_cast<__bf16>(static_cast<float>((3 * lane + i) & 1));
+  }
+  probe_f32x16 c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[i][r] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c[i][r];
+  out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = s;
+}
+
 }  // namespace
 
 }  // namespace bitlinear
@@ -119,6 +150,14 @@ int bitlinear_probe_mfma_i8(int iters, int blocks, int32_t* out, void* stream) {
   if (iters < 1 || blocks < 1 || blocks > (1 << 20)) return BITLINEAR_PROBE_ERR_SHAPE;
   if (!aligned(out, 4)) return BITLINEAR_PROBE_ERR_ALIGN;
   bitlinear::mfma_i8_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, out);
+  return hip_status(hipGetLastError());
+}
+
+int bitlinear_probe_mfma_bf16(int iters, int blocks, float* out, void* stream) {
+  if (!out) return BITLINEAR_PROBE_ERR_NULL;
+  if (iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > (1 << 20)) return BITLINEAR_PROBE_ERR_SHAPE;
+  if (!aligned(out, 4)) return BITLINEAR_PROBE_ERR_ALIGN;
+  bitlinear::mfma_bf16_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, out);
   return hip_status(hipGetLastError());
 }
 

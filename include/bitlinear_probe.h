@@ -2,9 +2,10 @@
  * bitlinear_probe.h -- attainable-peak probes for the BitLinear benchmark.
  *
  * A separate library (libbitlinear_probe.so), not part of the BitLinear ABI in
- * bitlinear.h: two plain kernels that measure what the GPU delivers to simple
+ * bitlinear.h: plain kernels that measure what the GPU delivers to simple
  * code, reported by the benchmark beside the published MI355X peaks (8 TB/s
- * HBM3E, 5 POPS dense INT8) that the roofline fractions use.
+ * HBM3E, 5 POPS dense INT8, 2.5 PFLOP/s dense bf16) that the roofline
+ * fractions use.
  *
  * Pointers are device pointers owned by the caller; `stream` is a hipStream_t
  * passed as void*; calls only enqueue work.  Arguments are checked on the host
@@ -46,6 +47,16 @@ int bitlinear_probe_stream(const void* src, void* dst, int64_t bytes, int blocks
  * blocks * 4 * 8 * iters * 65536.  Requires iters >= 1, 1 <= blocks <= 2^20.
  */
 int bitlinear_probe_mfma_i8(int iters, int blocks, int32_t* out, void* stream);
+
+/*
+ * The same with v_mfma_f32_32x32x16_bf16 (32768 floating-point operations
+ * each) on eight independent float32 accumulators, against the 2.5 PFLOP/s
+ * dense bf16 peak; operands are small integers, so `out` (blocks * 256 float)
+ * is exact and the same on every call.  Operations per call:
+ * blocks * 4 * 8 * iters * 32768.  Requires 1 <= iters <= 2^20,
+ * 1 <= blocks <= 2^20.
+ */
+int bitlinear_probe_mfma_bf16(int iters, int blocks, float* out, void* stream);
 
 #ifdef __cplusplus
 }

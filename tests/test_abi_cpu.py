@@ -44,7 +44,7 @@ def test_probe_library_is_separate(lib):
     BitLinear library neither declares nor exports them."""
     probe = abi.load_probe()
     names = declared_functions(PROBE_HEADER)
-    assert names == ["bitlinear_probe_mfma_i8", "bitlinear_probe_stream"]
+    assert names == ["bitlinear_probe_mfma_bf16", "bitlinear_probe_mfma_i8", "bitlinear_probe_stream"]
     for n in names:
         assert hasattr(probe, n), n
         assert n not in abi.SIGNATURES
@@ -305,6 +305,11 @@ def test_probe_checks(lib):
     assert m(1, 1, None, None) == abi.ERR_NULL
     assert m(0, 1, FAKE, None) == abi.ERR_SHAPE
     assert m(1, 0, FAKE, None) == abi.ERR_SHAPE
+    h = probe.bitlinear_probe_mfma_bf16
+    assert h(1, 1, None, None) == abi.ERR_NULL
+    assert h(0, 1, FAKE, None) == abi.ERR_SHAPE
+    assert h(1, 0, FAKE, None) == abi.ERR_SHAPE
+    assert h(1, 1, P(4098), None) == abi.ERR_ALIGN
 
 
 def test_header_documents_citations_and_conventions():

@@ -52,3 +52,28 @@ def test_probe_mfma_deterministic():
     bl.abi.check("probe", lib.bitlinear_probe_mfma_i8(7, 4, b.data_ptr(), stream()))
     torch.cuda.synchronize()
     assert torch.equal(a, b) and bool((a != 0).any())
+
+
+def test_probe_mfma_bf16_exact():
+    """Small-integer bf16 operands: every product and partial sum is exact,
+    so each thread's sum is a fixed value, the same on every call and equal
+    to the plain matrix product's (operands rebuilt from the lane pattern)."""
+    import numpy as np
+    lib = bl.abi.load_probe()
+    a = torch.empty(4 * 256, dtype=torch.float32, device=DEV)
+    b = torch.empty_like(a)
+    bl.abi.check("probe", lib.bitlinear_probe_mfma_bf16(5, 4, a.data_ptr(), stream()))
+    bl.abi.check("probe", lib.bitlinear_probe_mfma_bf16(5, 4, b.data_ptr(), stream()))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and bool((a != 0).any())
+    # one 32x32x16 product: lane l holds A[l % 32][8 (l / 32) + i] and B[8 (l / 32) + i][l % 32]
+    A = np.zeros((32, 16)); B = np.zeros((16, 32))
+    for l in range(64):
+        for i in range(8):
+            A[l % 32, 8 * (l // 32) + i] = (l + i) & 3
+            B[8 * (l // 32) + i, l % 32] = (3 * l + i) & 1
+    C = A @ B  # lane l's 16 accumulator elements are 16 entries of column l % 32
+    # thread sum = 8 accumulators x 5 iterations x (its 16 entries of C); the
+    # total over a wave is 8 * 5 * C.sum()
+    got = a.cpu().numpy().reshape(4, 4, 64).sum(axis=2)  # per wave
+    assert np.allclose(got, 8 * 5 * C.sum())
