@@ -34,11 +34,12 @@
 //            of word j holds k = 20j + 4t + b for t = 0..4 as
 //            ceil(256 v / 243) with v = sum_t c_t 3^(4-t).  Multiplying the
 //            byte by 3 puts digit t = 0 in bits 8-9 and the rest, which yields
-//            the next digit the same way, in bits 0-7.  Bytes 0,2 and 1,3 of
-//            a word are processed as two 16-bit lanes per register, so one
-//            multiply, one mask and half a byte permute give four codes.  The
-//            twenty code dwords of a unit, in (word, digit) order, are k = 4f
-//            .. 4f+3 of the unit: five B operands for five MFMAs.
+//            the next digit the same way, in bits 0-7.  The four bytes of a
+//            word sit in the four 16-bit lanes of a register pair, so one
+//            64-bit shift-add (x + 2x), one byte permute and two masks give
+//            four codes.  The twenty code dwords of a unit, in (word, digit)
+//            order, are k = 4f .. 4f+3 of the unit: five B operands for five
+//            MFMAs.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -54,18 +55,25 @@ constexpr int kWaves = kDecodeThreads / kWave;
 constexpr int kNontemporal = 2;    // cache-policy bits of a buffer load: streaming
 
 // Radix-3 unpack of one word (20 weights): d[t] holds the offset codes of
-// k = 20j + 4t + b in byte b.
+// k = 20j + 4t + b in byte b.  Radix-3 decode is bound by the vector ALU, so
+// the times-3 step is one 64-bit shift-add over all four 16-bit lanes
+// (v_lshl_add_u64, written out: the compiler splits a 64-bit multiply of
+// masked lanes into two 32-bit ones).  A lane stays below 768, so no carry
+// crosses into the next lane.
 __device__ __forceinline__ void unpack_r3_word(uint32_t w, int* d) {
-  uint32_t e = w & 0x00ff00ffu;                             // bytes 0 and 2, one per 16-bit lane
-  uint32_t o = __builtin_amdgcn_perm(w, w, 0x0c030c01u);    // bytes 1 and 3 (selector 12 gives 0)
+  uint32_t lo = __builtin_amdgcn_perm(w, w, 0x0c010c00u);   // bytes 0, 1 in 16-bit lanes (selector 12 gives 0)
+  uint32_t hi = __builtin_amdgcn_perm(w, w, 0x0c030c02u);   // bytes 2, 3
 #pragma unroll
   for (int t = 0; t < 5; ++t) {
-    e *= 3u;  // lane < 768: digit in bits 8-9 of the lane, rest in bits 0-7
-    o *= 3u;
-    // bytes {e.1, o.1, e.3, o.3}: the codes of bytes 0, 1, 2, 3 of the word
-    d[t] = static_cast<int>(__builtin_amdgcn_perm(o, e, 0x07030501u));
-    e &= 0x00ff00ffu;
-    o &= 0x00ff00ffu;
+    uint64_t v = (static_cast<uint64_t>(hi) << 32) | lo;
+    asm volatile("v_lshl_add_u64 %0, %1, 1, %1" : "=v"(v) : "v"(v));  // v = 3 v
+    lo = static_cast<uint32_t>(v);
+    hi = static_cast<uint32_t>(v >> 32);
+    // digits in bits 8-9 of each lane: bytes {lo.1, lo.3, hi.1, hi.3} are
+    // the codes of bytes 0, 1, 2, 3 of the word
+    d[t] = static_cast<int>(__builtin_amdgcn_perm(hi, lo, 0x07050301u));
+    lo &= 0x00ff00ffu;  // the rest, for the next digit
+    hi &= 0x00ff00ffu;
   }
 }
 
@@ -129,8 +137,11 @@ __host__ __device__ inline int stage_bytes(int M, int groups, bool with_acc, int
 // rows and its four waves each walk a quarter of the rows' load chunks; the
 // exact INT32 partial sums are added in LDS (in any order: they are
 // integers) and one wave rescales and stores them.
+// Radix-3 is held to 128 registers (four waves per SIMD instead of three):
+// more waves keep its vector ALU busier.  The 2-bit form is bound by memory
+// and keeps the compiler's choice.
 template <int FMT, int DT, bool VEC, int EPI, bool SPLIT>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(FMT == 3 ? 4 : 1))) void decode_kernel(
     const void* __restrict__ X, int M, int64_t K, int64_t Kp, int64_t units,
     const uint32_t* __restrict__ packed, int64_t N, const float* __restrict__ gamma,
     float* __restrict__ Y, int32_t* __restrict__ acc, int blocks_per_layer, int groups,
@@ -160,7 +171,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   if constexpr (EPI == kEpiAcc) acc += layer * M * N;
   gamma += layer;
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar address math
   const int lane = threadIdx.x & (kWave - 1);
   const int j = lane & 15;
   const int g = lane >> 4;
@@ -206,20 +217,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
       // fewer operations: chunks before the last hold 4 units, so chunk cs of
       // lane (j, g) is at blk + 64 R cs + 16 (4 j + g), linear in cs; the last
       // chunk holds W = units - 4 last units (lanes j W + g, none for g >= W).
-      // (For the memory-bound 2-bit decode the general form below streams
-      // faster, so it keeps it.)
+      // The block part is wave-uniform (scalar), the lane part is one of two
+      // per-batch values: two vector operations per load.  (For the
+      // memory-bound 2-bit decode the general form below streams faster, so
+      // it keeps it.)
       const uint32_t cs0 = static_cast<uint32_t>(c_lo + cb * kUnroll);
-      const uint32_t base = blk + cs0 * R * 64u + (4u * j + g) * 16u;
       const uint32_t last = (units32 - 1u) >> 2;
       const uint32_t Wl = units32 - 4u * last;
+      // lane part of the offset: invalid lanes get the resource size, so
+      // that any valid block offset added to it stays past the end
+      const uint32_t nrec = static_cast<uint32_t>(N * units * 16);
+      const bool jr = static_cast<uint32_t>(j) < R;
+      const uint32_t l_full = jr ? (4u * j + g) * 16u : nrec;
+      const uint32_t l_last = jr && static_cast<uint32_t>(g) < Wl ? (j * Wl + g) * 16u : nrec;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const uint32_t cs = cs0 + static_cast<uint32_t>(u);
-        uint32_t off = base + static_cast<uint32_t>(u) * R * 64u;
-        if (cs == last) off = off - (4u * j + g) * 16u + (j * Wl + g) * 16u;
-        const bool ok = row_ok && cs <= last && (cs < last || g < Wl) &&
-                        (!SPLIT || cs < static_cast<uint32_t>(c_hi));
-        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, ok ? off : kOff, 0, kNontemporal);
+        const bool in = valid && cs <= last && (!SPLIT || cs < static_cast<uint32_t>(c_hi));
+        // block part 2^31 when not due: past every resource, and with a lane
+        // part below 2^31 the sum does not wrap around
+        const uint32_t ub = in ? blk + cs * R * 64u : 0x80000000u;
+        const uint32_t off = ub + (cs == last ? l_last : l_full);
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off, 0, kNontemporal);
         r[u] = make_uint4(v[0], v[1], v[2], v[3]);
       }
       return;
@@ -300,10 +319,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     for (int u = 0; u < kUnroll; ++u) {
       const int cs = c_lo + cb * kUnroll + u;
       if (SPLIT && cs >= c_hi) continue;  // past the wave's quarter (wave-uniform)
-      const uint32_t un = static_cast<uint32_t>(cs) * 4u + g;
       // units past the row end give all-zero operands, so any in-bounds
-      // activation codes may pair with them
-      const uint32_t abase = un < units32 ? kPerUnit * un : 0u;
+      // activation codes may pair with them (radix-3: the row's last unit,
+      // with one minimum and no multiply)
+      uint32_t abase;
+      if constexpr (FMT == 3) {
+        abase = min(static_cast<uint32_t>(cs) * (4u * kPerUnit) + kPerUnit * g, kPerUnit * (units32 - 1u));
+      } else {
+        const uint32_t un = static_cast<uint32_t>(cs) * 4u + g;
+        abase = un < units32 ? kPerUnit * un : 0u;
+      }
       v4i bop[kMfma];
       unit_operands<FMT>(r[u], bop);
 #pragma unroll
