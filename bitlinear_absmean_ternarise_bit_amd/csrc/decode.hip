@@ -257,6 +257,9 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
 
   uint4 buf0[kUnroll], buf1[kUnroll];
   load_batch(0, true, buf0);
+  // gamma is needed only by the epilogue; asked for now, its latency hides
+  // behind the weights' (a single-layer call has little else to hide it)
+  const float gm = gamma[0];
   __builtin_amdgcn_sched_barrier(0);
 
   if constexpr (DT == 2) {
@@ -299,7 +302,6 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   // rows that are never stored.
   const int8_t* arow = sxq + (j < M ? j : 0) * lds_stride;
   const v4i zero = {0, 0, 0, 0};
-  const float gm = gamma[0];
   v4i c = zero;
   // the lane's output tokens 4g + r are fixed: their code sums and rescale
   // factors gamma * gamma_A / 127 are formed once, not per row group
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   // and the loads of b + 2 go out (into b's buffer, whose codes are already
   // unpacked) before b's epilogue.  sched_barrier keeps the scheduler from
   // sinking loads into the work that follows them.
-  load_batch(1, 1 < nbatch, buf1);
+  if (nbatch > 1) load_batch(1, true, buf1);  // (a single-layer call often has one batch)
   __builtin_amdgcn_sched_barrier(0);
   int b = 0;
   for (; b + 1 < nbatch; b += 2) {

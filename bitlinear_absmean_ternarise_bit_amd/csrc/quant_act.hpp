@@ -13,6 +13,32 @@
 
 namespace bitlinear {
 
+// Wave reductions on the quantiser's critical path: within each row of 16
+// lanes by DPP moves (swap neighbours, swap pairs, mirror the half-rows,
+// mirror the row), then the four row results read as scalars.  Every lane
+// gets the result.  A maximum and an integer sum do not depend on the order.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float quant_wave_max(float v) {
+  v = fmaxf(v, __int_as_float(dpp<0xb1>(__float_as_int(v))));   // quad_perm 1,0,3,2
+  v = fmaxf(v, __int_as_float(dpp<0x4e>(__float_as_int(v))));   // quad_perm 2,3,0,1
+  v = fmaxf(v, __int_as_float(dpp<0x141>(__float_as_int(v))));  // row_half_mirror
+  v = fmaxf(v, __int_as_float(dpp<0x140>(__float_as_int(v))));  // row_mirror
+  const int b = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+__device__ __forceinline__ int quant_wave_sum(int v) {
+  v += dpp<0xb1>(v);
+  v += dpp<0x4e>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
 // DT: 0 = float32, 1 = bfloat16.  VEC: rows are 16-byte aligned and hold a
 // whole number of 16-byte chunks.
 template <int DT>
@@ -126,7 +152,7 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, 
         for (int i = 0; i < P; ++i) m = fmaxf(m, fabsf(f[i]));
         mx = (lane + u * kWave < nc) ? fmaxf(mx, m) : mx;
       }
-      mx = wave_max(mx);
+      mx = quant_wave_max(mx);
       const float s = __fdiv_rn(127.0f, __fadd_rn(mx, kEps));
       int sum = 0;
 #pragma unroll
@@ -136,7 +162,7 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, 
       }
       for (int64_t k = K + lane; k < Kp; k += kWave) dst[k] = 0;
       gamma_a = mx;
-      codesum = wave_sum(sum);
+      codesum = quant_wave_sum(sum);
       return;
     }
   }
@@ -166,11 +192,11 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, 
   } else {
     for (int64_t k = lane; k < K; k += kWave) mx = fmaxf(mx, fabsf(load_one<DT>(row, k)));
   }
-  mx = wave_max(mx);
+  mx = quant_wave_max(mx);
   const float s = __fdiv_rn(127.0f, __fadd_rn(mx, kEps));
 
   gamma_a = mx;
-  codesum = wave_sum(codes_pass<DT, VEC>(row, K, Kp, lane, dst, s));
+  codesum = quant_wave_sum(codes_pass<DT, VEC>(row, K, Kp, lane, dst, s));
 }
 
 }  // namespace bitlinear
