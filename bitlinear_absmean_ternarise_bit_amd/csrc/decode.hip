@@ -384,7 +384,11 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   // and the loads of b + 2 go out (into b's buffer, whose codes are already
   // unpacked) before b's epilogue.  sched_barrier keeps the scheduler from
   // sinking loads into the work that follows them.
-  if (nbatch > 1) load_batch(1, true, buf1);  // (a single-layer call often has one batch)
+  // A single-layer call (SPLIT) often has one batch: skip the second's
+  // loads.  The streaming form keeps them unconditional: behind a branch the
+  // compiler no longer knows how many loads are in flight in the loop and
+  // waits for all of them.
+  if (!SPLIT || nbatch > 1) load_batch(1, 1 < nbatch, buf1);
   __builtin_amdgcn_sched_barrier(0);
   int b = 0;
   for (; b + 1 < nbatch; b += 2) {
