@@ -136,11 +136,14 @@ __host__ __device__ inline int stage_bytes(int M, int groups, bool with_acc, int
 // single layer, token by token): a workgroup owns one block of 16 weight
 // rows and its four waves each walk a quarter of the rows' load chunks; the
 // exact INT32 partial sums are added in LDS (in any order: they are
-// integers) and one wave rescales and stores them.
+// integers) and one wave rescales and stores them.  SPLIT is then the loads
+// per lane per batch, 2 or 4 (a quarter of a 2048-weight row is two chunks,
+// and forming the addresses of unused slots costs time on the critical
+// path); 0 is the streaming form.
 // Radix-3 is held to 128 registers (four waves per SIMD instead of three):
 // more waves keep its vector ALU busier.  The 2-bit form is bound by memory
 // and keeps the compiler's choice.
-template <int FMT, int DT, bool VEC, int EPI, bool SPLIT>
+template <int FMT, int DT, bool VEC, int EPI, int SPLIT>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(FMT == 3 ? 4 : 1))) void decode_kernel(
     const void* __restrict__ X, int M, int64_t K, int64_t Kp, int64_t units,
     const uint32_t* __restrict__ packed, int64_t N, const float* __restrict__ gamma,
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int esize = DT == 0 ? 4 : DT == 1 ? 2 : 1;
   constexpr int kPerUnit = Format<FMT>::kPerUnit;
   constexpr int kMfma = Format<FMT>::kMfma;
-  constexpr int kUnroll = Format<FMT>::kUnroll;
+  constexpr int kUnroll = SPLIT ? SPLIT : Format<FMT>::kUnroll;
   // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2:
   // give each XCD a contiguous run of (layer, row block) pairs, so that the
   // workgroups of one layer share one L2 (its tokens, or the FFN hidden
@@ -485,7 +488,7 @@ hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed,
                      (split ? static_cast<size_t>(kDecodeThreads) * sizeof(v4i)
                             : static_cast<size_t>(kWaves) * stage_bytes(m, groups, with_acc, code_bytes));
   auto go = [&](auto split_tag) {
-    constexpr bool S = decltype(split_tag)::value;
+    constexpr int S = decltype(split_tag)::value;
     if constexpr (DT == 2) {
       decode_kernel<FMT, DT, VEC, kEpiY, S><<<blocks, kDecodeThreads, lds, stream>>>(
           X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, ga_in, rs_in);
@@ -501,8 +504,13 @@ hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed,
             X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, nullptr, nullptr);
     }
   };
-  if (split) go(std::true_type());
-  else go(std::false_type());
+  // split form: 2 loads per batch when a wave's quarter of a row is at most
+  // eight load chunks, else 4 (measured on single layers: K = 2048 and 8192
+  // are faster with 2, K = 11008 with 4)
+  const int64_t chunks = (units + 3) / 4;
+  if (split && (chunks + kWaves - 1) / kWaves <= 8) go(std::integral_constant<int, 2>());
+  else if (split) go(std::integral_constant<int, 4>());
+  else go(std::integral_constant<int, 0>());
   return hipGetLastError();
 }
 
