@@ -152,6 +152,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   extern __shared__ __align__(16) int8_t sxq[];
   __shared__ float s_ga[kDecodeMaxM];
   __shared__ int s_rs[kDecodeMaxM];
+  __shared__ float s_sc[kDecodeMaxM];  // (split form) gamma * gamma_A / 127 per token
 
   constexpr int esize = DT == 0 ? 4 : DT == 1 ? 2 : 1;
   constexpr int kPerUnit = Format<FMT>::kPerUnit;
@@ -283,8 +284,10 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       }
     }
     if (threadIdx.x < M) {
-      s_ga[threadIdx.x] = ga_in[layer * M + threadIdx.x];
+      const float ga = ga_in[layer * M + threadIdx.x];
+      s_ga[threadIdx.x] = ga;
       s_rs[threadIdx.x] = rs_in[layer * M + threadIdx.x];
+      if constexpr (SPLIT) s_sc[threadIdx.x] = __fdiv_rn(__fmul_rn(gm, ga), 127.0f);
     }
   } else {
     // phase A: AbsMax INT8 codes of every token into LDS (one wave per token)
@@ -296,6 +299,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       if (lane == 0) {
         s_ga[m] = ga;
         s_rs[m] = rs;
+        if constexpr (SPLIT) s_sc[m] = __fdiv_rn(__fmul_rn(gm, ga), 127.0f);
       }
     }
   }
@@ -315,15 +319,17 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     const int i = 4 * g + r;
     const int ic = i < M ? i : M - 1;
     tok_rs[r] = s_rs[ic];
-    tok_scale[r] = __fdiv_rn(__fmul_rn(gm, s_ga[ic]), 127.0f);
+    // (the split form forms the scales in phase A, off its critical path)
+    tok_scale[r] = SPLIT ? s_sc[ic] : __fdiv_rn(__fmul_rn(gm, s_ga[ic]), 127.0f);
   }
 
   auto mfma_batch = [&](int b, const uint4 (&r)[kUnroll]) {
     const int cb = b - (b / bpg) * bpg;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      // (split form: slots past the wave's quarter were loaded as zeros and
+      // contribute nothing; contracting them keeps the batch one block)
       const int cs = c_lo + cb * kUnroll + u;
-      if (SPLIT && cs >= c_hi) continue;  // past the wave's quarter (wave-uniform)
       // units past the row end give all-zero operands, so any in-bounds
       // activation codes may pair with them (radix-3: the row's last unit,
       // with one minimum and no multiply)
