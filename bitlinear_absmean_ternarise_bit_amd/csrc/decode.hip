@@ -290,17 +290,31 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       if constexpr (SPLIT) s_sc[threadIdx.x] = __fdiv_rn(__fmul_rn(gm, ga), 127.0f);
     }
   } else {
-    // phase A: AbsMax INT8 codes of every token into LDS (one wave per token)
-    for (int m = wave; m < M; m += kWaves) {
-      float ga;
-      int rs;
-      quantize_row_wave<DT, VEC>(static_cast<const char*>(X) + m * K * esize, K, Kp, lane,
-                                 sxq + m * lds_stride, ga, rs);
+    // phase A: AbsMax INT8 codes of every token into LDS (one wave per token;
+    // a wave with two or more tokens takes them two at a time, their loads
+    // in flight together)
+    auto keep = [&](int m, float ga, int rs) {
       if (lane == 0) {
         s_ga[m] = ga;
         s_rs[m] = rs;
         if constexpr (SPLIT) s_sc[m] = __fdiv_rn(__fmul_rn(gm, ga), 127.0f);
       }
+    };
+    const char* xb = static_cast<const char*>(X);
+    int m = wave;
+    for (; m + kWaves < M; m += 2 * kWaves) {
+      float ga[2];
+      int rs[2];
+      quantize_two_rows_wave<DT, VEC>(xb + m * K * esize, xb + (m + kWaves) * K * esize, K, Kp, lane,
+                                      sxq + m * lds_stride, sxq + (m + kWaves) * lds_stride, ga, rs);
+      keep(m, ga[0], rs[0]);
+      keep(m + kWaves, ga[1], rs[1]);
+    }
+    for (; m < M; m += kWaves) {
+      float ga;
+      int rs;
+      quantize_row_wave<DT, VEC>(xb + m * K * esize, K, Kp, lane, sxq + m * lds_stride, ga, rs);
+      keep(m, ga, rs);
     }
   }
   __syncthreads();

@@ -199,4 +199,55 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, 
   codesum = quant_wave_sum(codes_pass<DT, VEC>(row, K, Kp, lane, dst, s));
 }
 
+// Two rows by one wave, both held in registers: their loads go out together,
+// so the wave waits for one memory round trip instead of two.  Rows of more
+// than RC 16-byte chunks per lane are quantised one after the other.  The
+// codes, gamma_A and code sums are those of quantize_row_wave.
+template <int DT, bool VEC, int RC = 4>
+__device__ __forceinline__ void quantize_two_rows_wave(const void* __restrict__ row0, const void* __restrict__ row1,
+                                                       int64_t K, int64_t Kp, int lane, int8_t* __restrict__ dst0,
+                                                       int8_t* __restrict__ dst1, float (&gamma_a)[2], int (&codesum)[2]) {
+  constexpr int P = ActTraits<DT>::kPerChunk;
+  const int64_t nc = K / P;
+  if (!VEC || nc > RC * kWave) {
+    quantize_row_wave<DT, VEC, RC>(row0, K, Kp, lane, dst0, gamma_a[0], codesum[0]);
+    quantize_row_wave<DT, VEC, RC>(row1, K, Kp, lane, dst1, gamma_a[1], codesum[1]);
+    return;
+  }
+  const uint4* r4[2] = {static_cast<const uint4*>(row0), static_cast<const uint4*>(row1)};
+  int8_t* dst[2] = {dst0, dst1};
+  uint4 v[2][RC];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < RC; ++u) {
+      const int64_t c = lane + u * kWave;
+      v[t][u] = r4[t][c < nc ? c : nc - 1];
+    }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int u = 0; u < RC; ++u) {
+      float f[P];
+      chunk_to_f32<DT>(v[t][u], f);
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < P; ++i) m = fmaxf(m, fabsf(f[i]));
+      mx = (lane + u * kWave < nc) ? fmaxf(mx, m) : mx;
+    }
+    mx = quant_wave_max(mx);
+    const float s = __fdiv_rn(127.0f, __fadd_rn(mx, kEps));
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < RC; ++u) {
+      const int64_t c = lane + u * kWave;
+      if (c < nc) sum += quantize_chunk<DT>(v[t][u], s, dst[t] + c * P);
+    }
+    for (int64_t k = K + lane; k < Kp; k += kWave) dst[t][k] = 0;
+    gamma_a[t] = mx;
+    codesum[t] = quant_wave_sum(sum);
+  }
+}
+
 }  // namespace bitlinear
