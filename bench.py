@@ -695,16 +695,17 @@ def cpu_baseline_backward(P, seconds):
 
 # ---------------------------------------------------------------------------
 
-def attainable_peaks(torch, bl, dev, read_blocks: int = 2048, mfma_iters: int = 20000) -> dict:
+def attainable_peaks(torch, bl, dev, read_blocks=(1024, 2048), mfma_iters: int = 20000) -> dict:
     """The chip's attainable rates for plain kernels, beside the published peaks:
     a 1 GiB streaming read (16-byte nontemporal loads, one contiguous slice per
-    workgroup), a 512 MiB -> 512 MiB streaming copy, and back-to-back INT8
-    MFMAs on registers (two workgroups per CU)."""
+    workgroup; the faster of 4 and 8 workgroups per CU), a 512 MiB -> 512 MiB
+    streaming copy, and back-to-back INT8 and bf16 MFMAs on registers (two
+    workgroups per CU)."""
     lib = bl.abi.load_probe()
     stream = torch.cuda.current_stream(dev).cuda_stream
     nbytes = 1 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
-    out = torch.empty(read_blocks * 256, dtype=torch.int32, device=dev)
+    out = torch.empty(max(read_blocks) * 256, dtype=torch.int32, device=dev)
 
     def timed(fn, reps=10):
         for _ in range(2):
@@ -717,11 +718,11 @@ def attainable_peaks(torch, bl, dev, read_blocks: int = 2048, mfma_iters: int = 
     def call(name, st):
         bl.abi.check(name, st)
 
-    ms_read = timed(lambda: call("bitlinear_probe_stream", lib.bitlinear_probe_stream(
-        buf.data_ptr(), None, nbytes, read_blocks, out.data_ptr(), stream)))
+    ms_read = min(timed(lambda: call("bitlinear_probe_stream", lib.bitlinear_probe_stream(
+        buf.data_ptr(), None, nbytes, b, out.data_ptr(), stream))) for b in read_blocks)
     half = buf.view(2, -1)
-    ms_copy = timed(lambda: call("bitlinear_probe_stream", lib.bitlinear_probe_stream(
-        half[0].data_ptr(), half[1].data_ptr(), nbytes // 2, read_blocks // 2, None, stream)))
+    ms_copy = min(timed(lambda: call("bitlinear_probe_stream", lib.bitlinear_probe_stream(
+        half[0].data_ptr(), half[1].data_ptr(), nbytes // 2, b // 2, None, stream))) for b in read_blocks)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     mout = torch.empty(2 * cus * 256, dtype=torch.int32, device=dev)
     ms_mfma = timed(lambda: call("bitlinear_probe_mfma_i8", lib.bitlinear_probe_mfma_i8(
@@ -736,7 +737,7 @@ def attainable_peaks(torch, bl, dev, read_blocks: int = 2048, mfma_iters: int = 
             "hbm_copy_GBps": round(nbytes / ms_copy / 1e6, 1),
             "mfma_i8_TOPS": round(ops / ms_mfma / 1e9, 1),
             "mfma_bf16_TFLOPs": round(flops / ms_bf16 / 1e9, 1),
-            "note": "plain kernels on this GPU: 1 GiB streaming read; 512 MiB copy (GB/s of bytes read "
+            "note": "plain kernels on this GPU: 1 GiB streaming read (the faster of 4 and 8 workgroups per CU); 512 MiB copy (GB/s of bytes read "
                     "+ written); independent v_mfma_i32_32x32x32_i8, and v_mfma_f32_32x32x16_bf16, on "
                     "registers"}
 
