@@ -199,6 +199,46 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ row, 
   codesum = quant_wave_sum(codes_pass<DT, VEC>(row, K, Kp, lane, dst, s));
 }
 
+// A row of at most RC 16-byte chunks per lane, loaded into registers (its
+// loads can go out before other work), then quantised as quantize_row_wave
+// does.  Chunks past the row re-read its last chunk and are not used.
+template <int DT, int RC = 4>
+__device__ __forceinline__ void load_row_chunks(const void* __restrict__ row, int64_t nc, int lane, uint4 (&v)[RC]) {
+  const uint4* r4 = static_cast<const uint4*>(row);
+#pragma unroll
+  for (int u = 0; u < RC; ++u) {
+    const int64_t c = lane + u * kWave;
+    v[u] = r4[c < nc ? c : nc - 1];
+  }
+}
+template <int DT, int RC = 4>
+__device__ __forceinline__ void quantize_loaded_row(const uint4 (&v)[RC], int64_t nc, int64_t K, int64_t Kp,
+                                                    int lane, int8_t* __restrict__ dst, float& gamma_a,
+                                                    int& codesum) {
+  constexpr int P = ActTraits<DT>::kPerChunk;
+  float mx = 0.0f;
+#pragma unroll
+  for (int u = 0; u < RC; ++u) {
+    float f[P];
+    chunk_to_f32<DT>(v[u], f);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) m = fmaxf(m, fabsf(f[i]));
+    mx = (lane + u * kWave < nc) ? fmaxf(mx, m) : mx;
+  }
+  mx = quant_wave_max(mx);
+  const float s = __fdiv_rn(127.0f, __fadd_rn(mx, kEps));
+  int sum = 0;
+#pragma unroll
+  for (int u = 0; u < RC; ++u) {
+    const int64_t c = lane + u * kWave;
+    if (c < nc) sum += quantize_chunk<DT>(v[u], s, dst + c * P);
+  }
+  for (int64_t k = K + lane; k < Kp; k += kWave) dst[k] = 0;
+  gamma_a = mx;
+  codesum = quant_wave_sum(sum);
+}
+
 // Two rows by one wave, both held in registers: their loads go out together,
 // so the wave waits for one memory round trip instead of two.  Rows of more
 // than RC 16-byte chunks per lane are quantised one after the other.  The

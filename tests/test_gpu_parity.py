@@ -168,6 +168,13 @@ FORWARD_CASES = [
     (1, 65472, 64, "bf16", "decode"),       # the longest row the decode path holds on chip (Kp + 16 = 65488)
     (16, 3000, 333, "f32", "decode"),       # float32 rows over 4 KiB: the wave quantiser's two passes
     (7, 8192, 200, "f32", "decode"),        # 32 KiB float32 rows, seven tokens over four waves
+    # single calls whose token rows (at most 4 16-byte chunks per lane) are
+    # requested before the weights: one token per wave, then five to eight
+    # tokens (some waves with two), float32 rows at the 4 KiB limit
+    (3, 2048, 100, "bf16", "decode"),
+    (4, 1024, 64, "f32", "decode"),
+    (5, 512, 96, "bf16", "decode"),
+    (6, 1024, 40, "f32", "decode"),
 ]
 
 
