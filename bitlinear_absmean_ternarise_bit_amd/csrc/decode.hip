@@ -1,9 +1,10 @@
 // Decode path (M <= 16 tokens): one fused kernel per call.
 //
 //   phase A  each workgroup quantises the (few) tokens into LDS with the
-//            per-token AbsMax quantiser (one wave per token), or copies
-//            codes quantised beforehand (the FFN block's down projection,
-//            whose input rows are long and shared by all its workgroups);
+//            per-token AbsMax quantiser (one wave per token, a wave with two
+//            tokens loading both rows at once), or copies codes quantised
+//            beforehand (the FFN block's down projection, whose input rows
+//            are long and shared by all its workgroups);
 //   phase B  each wave streams the packed codes of 16 weight rows once from
 //            HBM (16 bytes per lane per load; the rows' interleaved order
 //            makes one load instruction one contiguous KiB), unpacks them in
