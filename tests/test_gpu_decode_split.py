@@ -56,10 +56,11 @@ def pool(L, M, K, N, seed, fmt="2bit"):
 # The split form loads 2 chunks per lane per batch while a wave's quarter of
 # a row is at most 8 load chunks (K <= 8192 for 2-bit weights) and 4 beyond:
 # K = 8192 and 8448 sit on either side, 11008 and 65472 take several batches
-# of 4 with a partial last one.
+# of 4 with a partial last one.  Six tokens give two waves two tokens each
+# (both rows loaded at once, in both forms).
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 2048), (8, 2048, 5632), (3, 1000, 200), (16, 4000, 129),
                                    (1, 65472, 64), (5, 9, 40), (4, 8192, 128), (1, 8448, 48),
-                                   (2, 11008, 96)])
+                                   (2, 11008, 96), (6, 1024, 96)])
 def test_split_form_equals_streaming_form(M, K, N):
     L = max(300, -(-2048 // max(1, (N + 63) // 64)))  # enough row blocks for the normal form
     say(f"decode split vs streaming M={M} K={K} N={N} (batch of {L})")
