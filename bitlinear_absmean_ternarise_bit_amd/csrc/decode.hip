@@ -148,7 +148,7 @@ template <int FMT, int DT, bool VEC, int EPI, int SPLIT>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(FMT == 3 ? 4 : 1))) void decode_kernel(
     const void* __restrict__ X, int M, int64_t K, int64_t Kp, int64_t units,
     const uint32_t* __restrict__ packed, int64_t N, const float* __restrict__ gamma,
-    float* __restrict__ Y, int32_t* __restrict__ acc, int blocks_per_layer, int groups,
+    float* __restrict__ Y, int32_t* __restrict__ acc, int blocks_per_layer, int groups, int interleave,
     const float* __restrict__ ga_in, const int32_t* __restrict__ rs_in) {
   extern __shared__ __align__(16) int8_t sxq[];
   __shared__ float s_ga[kDecodeMaxM];
@@ -180,8 +180,15 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const int lane = threadIdx.x & (kWave - 1);
   const int j = lane & 15;
   const int g = lane >> 4;
+  // Row group gi of this wave starts at row n_base + gi * g_step.  A
+  // workgroup owns 4 * groups consecutive blocks of 16 rows; each wave takes
+  // a contiguous quarter of them, or (interleave) every fourth block, so that
+  // the four waves stream adjacent KiB chunks of one region.
+  const int64_t wg_rows = static_cast<int64_t>(kWaves) * groups * kRowsPerWave;
   const int64_t n_base = SPLIT ? static_cast<int64_t>(rb) * kRowsPerWave
-                               : (static_cast<int64_t>(rb) * kWaves + wave) * groups * kRowsPerWave;
+                               : static_cast<int64_t>(rb) * wg_rows +
+                                     static_cast<int64_t>(wave) * (interleave ? kRowsPerWave : groups * kRowsPerWave);
+  const int64_t g_step = interleave ? kWaves * kRowsPerWave : kRowsPerWave;
   const int chunks = static_cast<int>((units + 3) >> 2);  // load instructions per row
   // the wave's load chunks of a row: all of them, or (SPLIT) its quarter
   const int c_lo = SPLIT ? wave * chunks / kWaves : 0;
@@ -213,7 +220,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   auto load_batch = [&](int b, bool valid, uint4 (&r)[kUnroll]) {
     const int gi = b / bpg;
     const int cb = b - gi * bpg;
-    const uint32_t n0 = static_cast<uint32_t>(n_base + gi * kRowsPerWave);
+    const uint32_t n0 = static_cast<uint32_t>(n_base + gi * g_step);
     const uint32_t R = N32 > n0 ? min(16u, N32 - n0) : 0u;  // rows of the block
     const uint32_t blk = n0 * units32 * 16u;
     const bool row_ok = valid && static_cast<uint32_t>(j) < R;
@@ -413,7 +420,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     const int gi = b / bpg;
     if (b - gi * bpg != bpg - 1) return;
     const int x = gi * kRowsPerWave + j;
-    const uint32_t n = static_cast<uint32_t>(n_base + x);
+    const uint32_t n = static_cast<uint32_t>(n_base + gi * g_step + j);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * g + r;
@@ -492,7 +499,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     // wave complete in order, so the staged values are visible here
     for (int i = 0; i < M; ++i) {
       for (int x = lane; x < wave_rows; x += kWave) {
-        const uint32_t n = static_cast<uint32_t>(n_base + x);
+        const uint32_t n = static_cast<uint32_t>(n_base + (x >> 4) * g_step + (x & 15));
         const uint32_t off = n < N32 ? (static_cast<uint32_t>(i) * N32 + n) * 4u : kOff;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out_y[i * wave_rows + x]), ysrc, off, 0, 0);
         if constexpr (EPI == kEpiAcc)
@@ -534,6 +541,11 @@ hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed,
   const bool split = L * bpl < kSplitBelow && blocks16 > bpl;
   if (split) bpl = static_cast<int>(blocks16);
   const unsigned blocks = static_cast<unsigned>(L * bpl);
+  // 2-bit weights, one workgroup per layer: the waves take interleaved row
+  // groups (1 x 2048 x 2048 layers in a batch: +1.0-1.5%, measured on four
+  // boxes; where several workgroups share a layer the contiguous quarters
+  // measured as fast or faster)
+  const int ilv = FMT == 2 && !split && bpl == 1 && groups > 1;
   const int m = static_cast<int>(M);
   const bool with_acc = acc != nullptr && !relu2;
   const int64_t code_bytes = M * (Kp + 16);
@@ -545,17 +557,17 @@ hipError_t launch_v(const void* X, int64_t M, int64_t K, const uint32_t* packed,
     constexpr int S = decltype(split_tag)::value;
     if constexpr (DT == 2) {
       decode_kernel<FMT, DT, VEC, kEpiY, S><<<blocks, kDecodeThreads, lds, stream>>>(
-          X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, ga_in, rs_in);
+          X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, ilv, ga_in, rs_in);
     } else {
       if (FMT == 2 && relu2)
         decode_kernel<FMT, DT, VEC, FMT == 2 ? kEpiRelu2 : kEpiY, S><<<blocks, kDecodeThreads, lds, stream>>>(
-            X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, nullptr, nullptr);
+            X, m, K, Kp, units, packed, N, gamma, Y, nullptr, bpl, groups, ilv, nullptr, nullptr);
       else if (acc)
         decode_kernel<FMT, DT, VEC, kEpiAcc, S><<<blocks, kDecodeThreads, lds, stream>>>(
-            X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, nullptr, nullptr);
+            X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, ilv, nullptr, nullptr);
       else
         decode_kernel<FMT, DT, VEC, kEpiY, S><<<blocks, kDecodeThreads, lds, stream>>>(
-            X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, nullptr, nullptr);
+            X, m, K, Kp, units, packed, N, gamma, Y, acc, bpl, groups, ilv, nullptr, nullptr);
     }
   };
   // split form: 2 loads per batch when a wave's quarter of a row is at most

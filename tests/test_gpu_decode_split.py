@@ -77,6 +77,23 @@ def test_split_form_equals_streaming_form(M, K, N):
             check_y(Ys.cpu().numpy(), ref["Y"])
 
 
+# Batches where one workgroup covers a whole layer, so its waves take every
+# fourth block of 16 rows: 600 layers of 2000 rows (32 blocks per wave, the
+# last three blocks past N) and 1100 layers of 1000 rows (16 per wave, the
+# last block half past N).
+@pytest.mark.parametrize("L,M,K,N", [(600, 2, 256, 2000), (1100, 3, 200, 1000)])
+def test_whole_layer_workgroups_ragged_rows(L, M, K, N):
+    say(f"decode batch of {L} whole-layer workgroups M={M} K={K} N={N}")
+    P, X, packed, gamma = pool(L, M, K, N, seed=L + N)
+    Yb = bl.forward_batched(X, packed, gamma, K)
+    for l in (0, 1, L // 2, L - 1):
+        Ys = bl.forward(X[l], packed[l], gamma[l:l + 1], K)
+        torch.cuda.synchronize()
+        assert torch.equal(Ys, Yb[l]), l
+    ref = O.bitlinear_forward(P.X, P.W)
+    check_y(Yb[0].cpu().numpy(), ref["Y"])
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 2048), (8, 2048, 5632), (7, 1000, 300), (1, 12000, 64)])
 def test_split_form_equals_streaming_form_radix3(M, K, N):
     L = 300
