@@ -104,6 +104,37 @@ def test_ffn_batched_layers():
             check_y(Y[l].cpu().numpy(), refs[l]["Y"])
 
 
+def test_ffn_batched_whole_layer_workgroups():
+    """600 blocks with F = Do = 1000: both projections' decode launches give
+    one workgroup a whole layer (its waves take every fourth block of 16 rows,
+    the last block half past the end); batched equals single-block calls bit
+    for bit, and sampled blocks match the oracle."""
+    L, M, D, F, Do = 600, 2, 256, 1000, 1000
+    g = torch.Generator(device=DEV)
+    g.manual_seed(600)
+    Wu = torch.randn((L, F, D), generator=g, device=DEV) * 0.02
+    Wd = torch.randn((L, Do, F), generator=g, device=DEV) * 0.03
+    X = torch.randn((L, M, D), generator=g, device=DEV).to(torch.bfloat16)
+    up = (torch.empty((L, F, bl.packed_words(D)), dtype=torch.int32, device=DEV),
+          torch.empty((L,), dtype=torch.float32, device=DEV))
+    down = (torch.empty((L, Do, bl.packed_words(F)), dtype=torch.int32, device=DEV),
+            torch.empty((L,), dtype=torch.float32, device=DEV))
+    for l in range(L):
+        bl.quantize_weights(Wu[l], out_packed=up[0][l], out_gamma=up[1][l:l + 1])
+        bl.quantize_weights(Wd[l], out_packed=down[0][l], out_gamma=down[1][l:l + 1])
+    Y, A = bl.ffn_forward(X, up, down, path="decode", return_hidden=True)
+    torch.cuda.synchronize()
+    for l in (0, 1, L // 2, L - 1):
+        Yl, Al = bl.ffn_forward(X[l], (up[0][l], up[1][l:l + 1]), (down[0][l], down[1][l:l + 1]),
+                                path="decode", return_hidden=True)
+        torch.cuda.synchronize()
+        assert torch.equal(Al, A[l]) and torch.equal(Yl, Y[l]), l
+    for l in (0, L - 1):
+        ref = O.ffn_forward(X[l].float().cpu().numpy(), Wu[l].cpu().numpy(), Wd[l].cpu().numpy())
+        assert np.array_equal(A[l].cpu().numpy(), ref["A"])
+        check_y(Y[l].cpu().numpy(), ref["Y"])
+
+
 def test_ffn_all_negative_preactivations_give_zero():
     X = np.abs(np.random.default_rng(3).standard_normal((4, 128))).astype(np.float32)
     Wu = -np.abs(np.random.default_rng(4).standard_normal((96, 128))).astype(np.float32) * 0.02
