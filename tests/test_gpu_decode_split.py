@@ -60,7 +60,7 @@ def pool(L, M, K, N, seed, fmt="2bit"):
 # (both rows loaded at once, in both forms).
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 2048), (8, 2048, 5632), (3, 1000, 200), (16, 4000, 129),
                                    (1, 65472, 64), (5, 9, 40), (4, 8192, 128), (1, 8448, 48),
-                                   (2, 11008, 96), (6, 1024, 96)])
+                                   (2, 11008, 96), (6, 1024, 96), (1, 1000, 200), (1, 64, 64)])
 def test_split_form_equals_streaming_form(M, K, N):
     L = max(300, -(-2048 // max(1, (N + 63) // 64)))  # enough row blocks for the normal form
     say(f"decode split vs streaming M={M} K={K} N={N} (batch of {L})")
@@ -75,6 +75,21 @@ def test_split_form_equals_streaming_form(M, K, N):
             ref = O.bitlinear_forward(P.X, P.W)
             assert np.array_equal(acc.cpu().numpy(), ref["acc"])
             check_y(Ys.cpu().numpy(), ref["Y"])
+
+
+# One token, whose row every wave quantises for its own quarter of K: float32
+# tokens (rows of up to 1024 values take that form) against the oracle, with
+# quarters that end inside a unit, inside the padding, or hold no codes.
+@pytest.mark.parametrize("K,N", [(1024, 300), (1000, 77), (200, 64), (9, 40)])
+def test_single_token_f32_per_wave_quarters(K, N):
+    say(f"decode single token f32 K={K} N={N}")
+    P = random_problem(1, K, N, seed=K + N, x_dtype="f32")
+    packed, gamma = bl.quantize_weights(torch.from_numpy(P.W).to(DEV))
+    Y, acc = bl.forward(torch.from_numpy(P.X).to(DEV), packed, gamma, K, return_acc=True)
+    torch.cuda.synchronize()
+    ref = O.bitlinear_forward(P.X, P.W)
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    check_y(Y.cpu().numpy(), ref["Y"])
 
 
 # Batches where one workgroup covers a whole layer, so its waves take every
