@@ -82,10 +82,10 @@ TRAFFIC = {
     # `bench.py --workload W [--format F] --steps 1 --warmup 1 --no-cpu-baseline`; scale
     # factors 2.0 (FETCH_SIZE) and 1.0 (WRITE_SIZE) from the 1 GiB copy of
     # `bench.py --copy-calibration` (524,300 KiB read, 1,048,576 KiB written).
-    "decode_m1_k2048_n2048": {"sources_sha": "070a2c726f2c7c09", "fetch_bytes": 1078214246, "write_bytes": 8393318},
-    "decode_ffn_up_m8_k2048_n5632": {"sources_sha": "070a2c726f2c7c09", "fetch_bytes": 1088587366, "write_bytes": 67223552},
-    "decode_m1_k2048_n2048/radix3": {"sources_sha": "070a2c726f2c7c09", "fetch_bytes": 1079871898, "write_bytes": 10330112},
-    "decode_ffn_up_m8_k2048_n5632/radix3": {"sources_sha": "070a2c726f2c7c09", "fetch_bytes": 1091135693, "write_bytes": 82722816},
+    "decode_m1_k2048_n2048": {"sources_sha": "611c60b56dc85fee", "fetch_bytes": 1078214246, "write_bytes": 8393318},
+    "decode_ffn_up_m8_k2048_n5632": {"sources_sha": "611c60b56dc85fee", "fetch_bytes": 1088587366, "write_bytes": 67223552},
+    "decode_m1_k2048_n2048/radix3": {"sources_sha": "611c60b56dc85fee", "fetch_bytes": 1079871898, "write_bytes": 10330112},
+    "decode_ffn_up_m8_k2048_n5632/radix3": {"sources_sha": "611c60b56dc85fee", "fetch_bytes": 1091135693, "write_bytes": 82722816},
     "decode_m1_k2048_n2048/lut": {"sources_sha": "6d4398590ebb1f5f", "fetch_bytes": 1076063744, "write_bytes": 8388608},
     "decode_ffn_up_m8_k2048_n5632/lut": {"sources_sha": "6d4398590ebb1f5f", "fetch_bytes": 1082523392, "write_bytes": 67223552},
     "prefill_ffn_m2048_k4096_n11008": {"sources_sha": "b4162daa313c2f73", "fetch_bytes": 117062656, "write_bytes": 90282240},
