@@ -188,6 +188,35 @@ def run_timed(args, torch, step, what: str):
     return ms, warmup, steps
 
 
+def sustained_obj(sus, units_per_step: float, unit: str, peak: float) -> dict:
+    ms, warmup, steps = sus
+    v = units_per_step / (ms * 1e-3)
+    return {"value": round(v, 2), "unit": unit, "ms_per_step": round(ms, 6), "frac": round(v / peak, 4),
+            "warmup": warmup, "steps": steps,
+            "note": "the same step timed again after the line's own timed region, once the GPU has run it "
+                    f"untimed for {SETTLE_S} s (the sustained state it reaches after ~0.15 s of load); "
+                    "the line's value keeps the counts given on the command line"}
+
+
+def sustained_after(args, torch, step, ms_step: float):
+    """With explicit --warmup / --steps (timed exactly as given, above): the same
+    step again after the default settling, as a second figure beside the line's
+    value: untimed for at least SETTLE_S seconds, then timed for at least
+    TIMED_S seconds.  None when the counts were already duration-based."""
+    if args.warmup is None or args.steps is None:
+        return None
+    est = max(ms_step * 1e-3, 1e-6)
+    warmup = min(100000, max(MIN_WARMUP, math.ceil(SETTLE_S / est)))
+    steps = min(100000, max(MIN_STEPS, math.ceil(TIMED_S / est)))
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    with Timer(torch) as t:
+        for _ in range(steps):
+            step()
+    return t.ms / steps, warmup, steps
+
+
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
@@ -286,6 +315,7 @@ def bench_decode(args, torch, bl, dev):
 
     ms_step, warmup, steps = run_timed(args, torch, step, "decode")
     step_bytes = L * (packed_bytes + M * K * 2 + M * N * 4)
+    sus = sustained_after(args, torch, step, ms_step)
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
     gw_s = L * N * K / (ms_step * 1e-3) / 1e9
     log(f"[bench] decode: {gbps:.1f} GB/s, {gw_s:.1f} G weights/s")
@@ -320,6 +350,7 @@ def bench_decode(args, torch, bl, dev):
                                 "decode_kernel (fused quantise + GEMV + rescale), one launch per step")},
         "weights_per_s": {"value": round(gw_s, 2), "unit": "G weights/s",
                           "note": "N*K*layers per step / step time: compares weight formats"},
+        **({"sustained": sustained_obj(sus, step_bytes / 1e9, "GB/s", HBM_PEAK_GBPS)} if sus else {}),
         "single_call": {"us": round(single_us, 2), "GBps": round(layer_bytes / (single_us * 1e-6) / 1e9, 2),
                         "us_graph": round(graph_us, 2),
                         "GBps_graph": round(layer_bytes / (graph_us * 1e-6) / 1e9, 2),
@@ -450,6 +481,7 @@ def bench_prefill(args, torch, bl, dev, workload=None):
             bl.forward_quantized(Xq, ga, rs, packed, gamma, K, out=Y)
     gemm_ms = tg.ms / steps
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    sus = sustained_after(args, torch, step, ms_step)
     step_bytes = N * bl.packed_words(K) * 4 + M * K * 2 + M * N * 4
     out = {
         "metric": METRIC, "value": round(tops, 2), "unit": "TOPS",
@@ -462,6 +494,7 @@ def bench_prefill(args, torch, bl, dev, workload=None):
                      "traffic": traffic_for(workload, "prefill"),
                      "kernel": "prefill_gemm_kernel (INT8 MFMA + fused rescale)",
                      "kernel_ms": round(gemm_ms, 6)},
+        **({"sustained": sustained_obj(sus, ops / 1e12, "TOPS", INT8_PEAK_TOPS)} if sus else {}),
         "weight_quantisation": {"ms_per_matrix": round(tq.ms, 4),
                                 "GBps": round((4 * N * K + N * bl.packed_words(K) * 4) / (tq.ms * 1e-3) / 1e9, 2),
                                 "note": "absmean + ternarise + pack, offline, not in the step"},

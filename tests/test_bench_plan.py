@@ -92,3 +92,23 @@ def test_run_timed_runs_exactly_the_planned_steps():
     assert (warmup, steps) == (4, 9)
     assert clock.calls == 4 + 9
     assert ms == pytest.approx(2.0)
+
+
+def test_sustained_figure_only_after_explicit_counts():
+    # explicit counts: the line's value is the exact K-step timing, and the
+    # same step is timed again after the default settling, as a second figure
+    clock = _Clock(170e-6)
+    ms, warmup, steps = bench.run_timed(_args(5, 20), _Torch(clock), clock.step, "stub")
+    assert clock.calls == 25
+    sus = bench.sustained_after(_args(5, 20), _Torch(clock), clock.step, ms)
+    ms2, w2, s2 = sus
+    assert w2 * 170e-6 >= bench.SETTLE_S * (1 - 1e-9) and s2 * 170e-6 >= bench.TIMED_S * (1 - 1e-9)
+    assert clock.calls == 25 + w2 + s2
+    assert ms2 == pytest.approx(0.17)
+    obj = bench.sustained_obj(sus, 1.0, "GB/s", 8000.0)
+    assert obj["value"] == pytest.approx(1.0 / 170e-6, rel=1e-4) and obj["warmup"] == w2 and obj["steps"] == s2
+    # duration-based counts already: no second figure, nothing run
+    clock = _Clock(170e-6)
+    assert bench.sustained_after(_args(), _Torch(clock), clock.step, 0.17) is None
+    assert bench.sustained_after(_args(warmup=5), _Torch(clock), clock.step, 0.17) is None
+    assert clock.calls == 0
